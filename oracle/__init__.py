@@ -1,0 +1,119 @@
+"""CPU oracle for the fused LiteLinear forward -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library and its Python binding
+never import it, and it imports nothing from them.
+
+It wraps ``litelinear_oracle.c`` (plain C, float64, exact e4m3fn decode by
+the closed form of the OCP format) through ctypes.  The forward it computes is
+the equation in the introduction of the LiteLinear README (page
+"moonmath-ai/LiteLinear"):
+
+    y = (x B^T) A^T + scale * (x dec(Q)^T) + bias
+
+with A [out, r], B [r, in] and Q [out, in] as the README's Features list and
+the tt_compressor page's ``SVDLinearLayer`` lay them out.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+from . import build as _build
+
+_LIB = None
+
+
+def library(path: str | None = None):
+    """Load (building on first use) the oracle's shared library."""
+    global _LIB
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _LIB = _bind(ctypes.CDLL(_build.LIB))
+    return _LIB
+
+
+def _bind(lib):
+    lib.oracle_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3fn_to_f64.restype = ctypes.c_double
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = ctypes.c_double
+    lib.oracle_decode_e4m3fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.oracle_decode_e4m3fn.restype = None
+    lib.oracle_forward_rows.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_forward_rows.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _bits16(t: torch.Tensor | None) -> np.ndarray | None:
+    if t is None:
+        return None
+    assert t.dtype == torch.bfloat16, t.dtype
+    return np.ascontiguousarray(t.detach().cpu().contiguous().view(torch.int16).numpy()).view(np.uint16)
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def decode_e4m3fn(codes, lib=None) -> np.ndarray:
+    """e4m3fn codes (any integer array or uint8 tensor) -> float64 values."""
+    lib = lib or library()
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.int64).astype(np.uint8))
+    out = np.empty(c.shape, np.float64)
+    lib.oracle_decode_e4m3fn(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def forward(x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,
+            Q: torch.Tensor, scale: float, bias: torch.Tensor | None,
+            rows=None, threads: int | None = None, want_T: bool = False, lib=None):
+    """float64 forward for all rows of x, or for the row indices in ``rows``.
+
+    x bf16 [M, in]; A bf16 [out, r]; B bf16 [r, in]; Q uint8 e4m3fn codes
+    [out, in]; scale a float32 value; bias bf16 [out] or None.  Returns y as
+    float64 [len(rows), out], plus T [len(rows), r] when ``want_T``.
+    """
+    lib = lib or library()
+    M, K = x.shape
+    N = Q.shape[0]
+    r = 0 if A is None else A.shape[1]
+    assert Q.shape == (N, K) and Q.dtype == torch.uint8
+    if r:
+        assert A.shape == (N, r) and B.shape == (r, K)
+    xb, Ab, Bb, bb = _bits16(x), _bits16(A) if r else None, _bits16(B) if r else None, _bits16(bias)
+    Qb = np.ascontiguousarray(Q.detach().cpu().contiguous().numpy())
+    if rows is None:
+        ridx = None
+        nrows = M
+    else:
+        ridx = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = ridx.size
+    y = np.empty((nrows, N), np.float64)
+    T = np.empty((nrows, max(r, 1)), np.float64) if want_T else None
+    rc = lib.oracle_forward_rows(_ptr(xb), _ptr(Ab), _ptr(Bb), _ptr(Qb), ctypes.c_float(scale),
+                                 _ptr(bb), M, K, N, r, _ptr(ridx), nrows, _ptr(y), _ptr(T),
+                                 int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_forward_rows rejected its arguments")
+    if want_T:
+        return y, T[:, :r]
+    return y
