@@ -1,0 +1,138 @@
+/*
+ * litelinear.h -- C ABI of the fused LiteLinear forward for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (LiteLinear README, page "moonmath-ai/LiteLinear": the
+ * equation in the introduction, and the Features list):
+ *
+ *     y = (x B^T) A^T + scale * (x dec(Q)^T) + bias
+ *
+ * i.e. a linear layer whose weight is held as W ~ A B + scale * dec(Q): a
+ * bf16 rank-r pair A [out, r], B [r, in] (the layout of SVDLinearLayer on the
+ * tt_compressor page) plus a residual Q stored as OCP e4m3fn codes with one
+ * per-tensor dequantisation multiplier `scale` (the README's state key
+ * Q_scale_inv).  Activations x are bf16 [M, in] (all leading dimensions of
+ * the caller's tensor flattened into M rows); y is bf16 [M, out].
+ *
+ * Conventions for every entry point:
+ *   - All matrices are dense, row-major, with leading dimension equal to the
+ *     row length.  Pointers are device pointers on the handle's device.
+ *   - The caller owns every tensor.  The library never frees them and does
+ *     not keep them past the point where the stream passes the call.
+ *   - Nothing throws or aborts across this ABI; every call returns a status.
+ *   - A kernel fault shows up as a HIP error at the caller's next
+ *     synchronisation, not as a status of the call that queued it.
+ */
+#ifndef LITELINEAR_H
+#define LITELINEAR_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct litelinear_ctx *litelinear_handle_t; /* opaque, library-owned */
+
+typedef enum {
+    LITELINEAR_OK = 0,
+    LITELINEAR_ERR_INVALID_ARG = 1, /* NULL required pointer, negative size, y overlapping an input */
+    LITELINEAR_ERR_UNSUPPORTED = 2, /* in % 16 != 0, or x / Q / B / y not 16-byte aligned */
+    LITELINEAR_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+    LITELINEAR_ERR_OOM = 4          /* workspace allocation failed */
+} litelinear_status_t;
+
+/* Options set per handle with litelinear_set_option(). */
+typedef enum {
+    /* Kernel family.  0 = choose from M (default); 1 = the skinny split-K
+     * kernel (HBM-bound on Q, for small M); 2 = the tiled kernel (MFMA-bound,
+     * for large M).  Both compute the same operation. */
+    LITELINEAR_OPT_PATH = 1,
+    /* Output type.  0 = bf16 y (default, rounded to nearest even);
+     * 1 = float32 y [M, out] (no output rounding; y must hold 4*M*out bytes). */
+    LITELINEAR_OPT_OUTPUT_F32 = 2,
+    /* Skinny path K-split count.  0 = choose automatically, else the number
+     * of slices of `in` (clamped to [1, in/64]). */
+    LITELINEAR_OPT_SPLIT_K = 3,
+    /* Per-kernel timing.  1 = record a HIP event pair around every kernel
+     * the handle launches, on the caller's stream; read the totals with
+     * litelinear_kernel_time().  0 = off (default). */
+    LITELINEAR_OPT_PROFILE = 4
+} litelinear_option_t;
+
+/* Kernels whose time litelinear_kernel_time() reports. */
+typedef enum {
+    LITELINEAR_KERNEL_LOWRANK_PROJ = 0, /* T = x B^T (tiled path) */
+    LITELINEAR_KERNEL_MAIN = 1,         /* the fused residual + rank-r + bias kernel (tiled path) */
+    LITELINEAR_KERNEL_SKINNY = 2        /* the skinny split-K kernel */
+} litelinear_kernel_t;
+
+/*
+ * Create a handle bound to HIP device `device_ordinal`.  The handle owns the
+ * workspace (the T = x B^T buffer of the tiled path, the split-K partial sums
+ * and counters of the skinny path); it grows on demand inside
+ * litelinear_forward.  One handle must not be used by two streams at once.
+ * Errors: INVALID_ARG (out == NULL or no such device), HIP, OOM.
+ */
+litelinear_status_t litelinear_create(litelinear_handle_t *out, int device_ordinal);
+
+/*
+ * y = (x B^T) A^T + scale * (x dec(Q)^T) + bias, queued on `stream`.
+ *
+ *   x     bf16  [M, in]   16-byte aligned.
+ *   A     bf16  [out, r]  may be NULL iff r == 0.
+ *   B     bf16  [r, in]   16-byte aligned; may be NULL iff r == 0.
+ *   Q     uint8 [out, in] OCP e4m3fn codes (bias 7, max 448, NaN 0x7F/0xFF),
+ *                         16-byte aligned.  Every code is decoded exactly.
+ *   scale float32 dequantisation multiplier: residual = scale * dec(Q).
+ *   bias  bf16  [out] or NULL (no bias).
+ *   y     bf16  [M, out] (float32 with LITELINEAR_OPT_OUTPUT_F32),
+ *                         16-byte aligned; must not overlap any input.
+ *   M, in, out, r  sizes; M == 0 or out == 0 returns OK without a launch.
+ *   stream  HIP stream of the handle's device (NULL = default stream).
+ *
+ * Precision: products in bf16 x bf16 (every e4m3fn value is exact in bf16)
+ * with float32 accumulation; T = x B^T is rounded once to bf16 before the
+ * rank-r product; y is rounded once (nearest even) to bf16.
+ * The call returns without synchronising; inputs must stay valid until the
+ * stream passes it.  Errors: INVALID_ARG, UNSUPPORTED, HIP, OOM.
+ */
+litelinear_status_t litelinear_forward(litelinear_handle_t h,
+                                       const void *x, const void *A, const void *B,
+                                       const void *Q, float scale, const void *bias,
+                                       void *y, int64_t M, int64_t in, int64_t out,
+                                       int64_t r, hipStream_t stream);
+
+/* Frees the handle and its workspace (synchronising the device first).
+ * NULL is accepted. */
+litelinear_status_t litelinear_destroy(litelinear_handle_t h);
+
+/* Host-only validation of litelinear_forward's arguments, with the same
+ * result codes; touches no device (usable without a GPU).  y_bytes_per_elem
+ * is 2 for bf16 output, 4 for float32 output. */
+litelinear_status_t litelinear_check_args(const void *x, const void *A, const void *B,
+                                          const void *Q, const void *bias, const void *y,
+                                          int64_t M, int64_t in, int64_t out, int64_t r,
+                                          int y_bytes_per_elem);
+
+/* Set an option (litelinear_option_t).  Errors: INVALID_ARG for an unknown
+ * key or value. */
+litelinear_status_t litelinear_set_option(litelinear_handle_t h, int key, int64_t value);
+
+/* Accumulated GPU time and launch count of one kernel kind since the last
+ * reset, measured with HIP events while LITELINEAR_OPT_PROFILE is on.
+ * Synchronises on the recorded events.  reset != 0 clears the totals. */
+litelinear_status_t litelinear_kernel_time(litelinear_handle_t h, int kernel,
+                                           double *total_ms, int64_t *launches, int reset);
+
+/* Static text for a status code. */
+const char *litelinear_status_string(litelinear_status_t s);
+
+/* Version string of the library ("major.minor.patch"). */
+const char *litelinear_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LITELINEAR_H */

@@ -1,0 +1,323 @@
+// C ABI of the fused LiteLinear forward (declared in include/litelinear.h):
+// argument checks, the per-handle workspace, the choice between the skinny
+// and the tiled kernels, and optional per-kernel event timing.
+#include "litelinear.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kNumKernels = 3;
+// Largest M sent to the skinny kernel when the path is chosen automatically.
+constexpr int64_t kSkinnyAutoMaxM = 64;
+
+struct Prof {
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+    double total_ms = 0.0;
+    int64_t launches = 0;
+};
+
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev) {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) {
+            err = hipSetDevice(dev);
+            changed = err == hipSuccess;
+        }
+    }
+    ~DeviceGuard() {
+        if (changed) (void)hipSetDevice(prev);
+    }
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool aligned(const void *p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+}  // namespace
+
+struct litelinear_ctx {
+    int device = 0;
+    void *t_ws = nullptr;
+    size_t t_ws_bytes = 0;
+    float *partials = nullptr;
+    size_t partials_bytes = 0;
+    unsigned *counters = nullptr;
+    size_t n_counters = 0;
+    int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0;
+    Prof prof[kNumKernels];
+    std::vector<hipEvent_t> event_pool;
+};
+
+namespace {
+
+litelinear_status_t grow(void **p, size_t *have, size_t need, bool zero) {
+    if (*have >= need) return LITELINEAR_OK;
+    if (*p) {
+        if (hipDeviceSynchronize() != hipSuccess) return LITELINEAR_ERR_HIP;
+        (void)hipFree(*p);
+        *p = nullptr;
+        *have = 0;
+    }
+    if (hipMalloc(p, need) != hipSuccess) {
+        *p = nullptr;
+        (void)hipGetLastError();
+        return LITELINEAR_ERR_OOM;
+    }
+    if (zero && hipMemset(*p, 0, need) != hipSuccess) return LITELINEAR_ERR_HIP;
+    *have = need;
+    return LITELINEAR_OK;
+}
+
+hipEvent_t take_event(litelinear_ctx *h) {
+    if (!h->event_pool.empty()) {
+        hipEvent_t e = h->event_pool.back();
+        h->event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Launches `fn` on `s`, bracketed by an event pair when profiling is on.
+template <class F>
+litelinear_status_t timed_launch(litelinear_ctx *h, int kind, hipStream_t s, F fn) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (h->opt_profile) {
+        e0 = take_event(h);
+        e1 = take_event(h);
+        if (!e0 || !e1 || hipEventRecord(e0, s) != hipSuccess) return LITELINEAR_ERR_HIP;
+    }
+    if (fn() != hipSuccess) return LITELINEAR_ERR_HIP;
+    if (h->opt_profile) {
+        if (hipEventRecord(e1, s) != hipSuccess) return LITELINEAR_ERR_HIP;
+        h->prof[kind].pending.emplace_back(e0, e1);
+    }
+    return LITELINEAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *litelinear_version(void) { return "0.1.0"; }
+
+const char *litelinear_status_string(litelinear_status_t s) {
+    switch (s) {
+        case LITELINEAR_OK: return "ok";
+        case LITELINEAR_ERR_INVALID_ARG: return "invalid argument";
+        case LITELINEAR_ERR_UNSUPPORTED: return "unsupported shape or alignment";
+        case LITELINEAR_ERR_HIP: return "HIP runtime error";
+        case LITELINEAR_ERR_OOM: return "out of device memory";
+    }
+    return "unknown status";
+}
+
+litelinear_status_t litelinear_check_args(const void *x, const void *A, const void *B, const void *Q,
+                                          const void *bias, const void *y, int64_t M, int64_t in,
+                                          int64_t out, int64_t r, int y_bytes_per_elem) {
+    const int64_t lim = (int64_t)1 << 40;
+    if (M < 0 || in < 0 || out < 0 || r < 0) return LITELINEAR_ERR_INVALID_ARG;
+    if (y_bytes_per_elem != 2 && y_bytes_per_elem != 4) return LITELINEAR_ERR_INVALID_ARG;
+    if (M > lim || in > lim || out > lim || r > lim) return LITELINEAR_ERR_INVALID_ARG;
+    if ((double)M * (double)in > 4.0e18 || (double)M * (double)out > 1.0e18 ||
+        (double)out * (double)in > 4.0e18 || (double)r * (double)(in + out) > 4.0e18)
+        return LITELINEAR_ERR_INVALID_ARG;
+    if (M == 0 || out == 0) return LITELINEAR_OK;  // nothing to compute
+    if (!y) return LITELINEAR_ERR_INVALID_ARG;
+    if (in > 0 && (!x || !Q)) return LITELINEAR_ERR_INVALID_ARG;
+    if (r > 0 && (!A || (in > 0 && !B))) return LITELINEAR_ERR_INVALID_ARG;
+    if (in % 16 != 0) return LITELINEAR_ERR_UNSUPPORTED;
+    if (in > 0 && (!aligned(x, 16) || !aligned(Q, 16))) return LITELINEAR_ERR_UNSUPPORTED;
+    if (r > 0 && in > 0 && !aligned(B, 16)) return LITELINEAR_ERR_UNSUPPORTED;
+    if (r > 0 && !aligned(A, 2)) return LITELINEAR_ERR_UNSUPPORTED;
+    if (bias && !aligned(bias, 2)) return LITELINEAR_ERR_UNSUPPORTED;
+    if (!aligned(y, (uintptr_t)y_bytes_per_elem)) return LITELINEAR_ERR_UNSUPPORTED;
+    const uint64_t ny = (uint64_t)M * (uint64_t)out * (uint64_t)y_bytes_per_elem;
+    if (overlaps(y, ny, x, (uint64_t)M * in * 2) || overlaps(y, ny, Q, (uint64_t)out * in) ||
+        (r > 0 && (overlaps(y, ny, A, (uint64_t)out * r * 2) || overlaps(y, ny, B, (uint64_t)r * in * 2))) ||
+        overlaps(y, ny, bias, (uint64_t)out * 2))
+        return LITELINEAR_ERR_INVALID_ARG;
+    return LITELINEAR_OK;
+}
+
+litelinear_status_t litelinear_create(litelinear_handle_t *out, int device_ordinal) {
+    if (!out) return LITELINEAR_ERR_INVALID_ARG;
+    *out = nullptr;
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess) {
+        (void)hipGetLastError();
+        return LITELINEAR_ERR_HIP;
+    }
+    if (device_ordinal < 0 || device_ordinal >= n) return LITELINEAR_ERR_INVALID_ARG;
+    litelinear_ctx *h = new (std::nothrow) litelinear_ctx();
+    if (!h) return LITELINEAR_ERR_OOM;
+    h->device = device_ordinal;
+    *out = h;
+    return LITELINEAR_OK;
+}
+
+litelinear_status_t litelinear_destroy(litelinear_handle_t h) {
+    if (!h) return LITELINEAR_OK;
+    litelinear_status_t st = LITELINEAR_OK;
+    {
+        DeviceGuard g(h->device);
+        if (hipDeviceSynchronize() != hipSuccess) st = LITELINEAR_ERR_HIP;
+        if (h->t_ws) (void)hipFree(h->t_ws);
+        if (h->partials) (void)hipFree(h->partials);
+        if (h->counters) (void)hipFree(h->counters);
+        for (auto &p : h->prof)
+            for (auto &e : p.pending) {
+                (void)hipEventDestroy(e.first);
+                (void)hipEventDestroy(e.second);
+            }
+        for (hipEvent_t e : h->event_pool) (void)hipEventDestroy(e);
+    }
+    delete h;
+    return st;
+}
+
+litelinear_status_t litelinear_set_option(litelinear_handle_t h, int key, int64_t value) {
+    if (!h) return LITELINEAR_ERR_INVALID_ARG;
+    switch (key) {
+        case LITELINEAR_OPT_PATH:
+            if (value < 0 || value > 2) return LITELINEAR_ERR_INVALID_ARG;
+            h->opt_path = value;
+            return LITELINEAR_OK;
+        case LITELINEAR_OPT_OUTPUT_F32:
+            if (value != 0 && value != 1) return LITELINEAR_ERR_INVALID_ARG;
+            h->opt_out_f32 = value;
+            return LITELINEAR_OK;
+        case LITELINEAR_OPT_SPLIT_K:
+            if (value < 0 || value > 65535) return LITELINEAR_ERR_INVALID_ARG;
+            h->opt_split = value;
+            return LITELINEAR_OK;
+        case LITELINEAR_OPT_PROFILE:
+            if (value != 0 && value != 1) return LITELINEAR_ERR_INVALID_ARG;
+            h->opt_profile = value;
+            return LITELINEAR_OK;
+    }
+    return LITELINEAR_ERR_INVALID_ARG;
+}
+
+litelinear_status_t litelinear_kernel_time(litelinear_handle_t h, int kernel, double *total_ms,
+                                           int64_t *launches, int reset) {
+    if (!h || kernel < 0 || kernel >= kNumKernels) return LITELINEAR_ERR_INVALID_ARG;
+    Prof &p = h->prof[kernel];
+    litelinear_status_t st = LITELINEAR_OK;
+    for (auto &e : p.pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(e.second) != hipSuccess || hipEventElapsedTime(&ms, e.first, e.second) != hipSuccess)
+            st = LITELINEAR_ERR_HIP;
+        p.total_ms += ms;
+        p.launches += 1;
+        h->event_pool.push_back(e.first);
+        h->event_pool.push_back(e.second);
+    }
+    p.pending.clear();
+    if (total_ms) *total_ms = p.total_ms;
+    if (launches) *launches = p.launches;
+    if (reset) {
+        p.total_ms = 0.0;
+        p.launches = 0;
+    }
+    return st;
+}
+
+litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, const void *A, const void *B,
+                                       const void *Q, float scale, const void *bias, void *y, int64_t M,
+                                       int64_t in, int64_t out, int64_t r, hipStream_t stream) {
+    if (!h) return LITELINEAR_ERR_INVALID_ARG;
+    const bool out_f32 = h->opt_out_f32 != 0;
+    litelinear_status_t st = litelinear_check_args(x, A, B, Q, bias, y, M, in, out, r, out_f32 ? 4 : 2);
+    if (st != LITELINEAR_OK) return st;
+    if (M == 0 || out == 0) return LITELINEAR_OK;
+    DeviceGuard guard(h->device);
+    if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
+
+    const int64_t r_pad = r > 0 ? cdiv(r, 64) * 64 : 0;
+    int64_t path = h->opt_path;
+    if (path == 0) path = (in > 0 && M <= kSkinnyAutoMaxM && ll::skinny_supports(M, r_pad)) ? 1 : 2;
+    if (path == 1 && (in == 0 || !ll::skinny_supports(M, r_pad))) return LITELINEAR_ERR_UNSUPPORTED;
+
+    if (path == 1) {
+        const int64_t ksteps = cdiv(in, 64);
+        int64_t splits = h->opt_split > 0 ? h->opt_split : ll::choose_skinny_splits(M, in, out);
+        if (splits > ksteps) splits = ksteps;
+        if (splits < 1) splits = 1;
+        const int64_t k_slice = cdiv(ksteps, splits) * 64;
+        splits = cdiv(in, k_slice);
+        const int64_t tiles_n = cdiv(out, ll::skinny_col_tile());
+        ll::SkinnyProblem p{};
+        p.x = x;
+        p.A = A;
+        p.B = B;
+        p.Q = Q;
+        p.bias = bias;
+        p.y = y;
+        p.scale = scale;
+        p.M = M;
+        p.K = in;
+        p.N = out;
+        p.r = r;
+        p.r_pad = r_pad;
+        p.splits = (int)splits;
+        p.k_slice = k_slice;
+        p.out_f32 = out_f32;
+        if (splits > 1) {
+            st = grow((void **)&h->partials, &h->partials_bytes, (size_t)splits * M * out * sizeof(float), false);
+            if (st != LITELINEAR_OK) return st;
+            size_t cbytes = h->n_counters * sizeof(unsigned);
+            st = grow((void **)&h->counters, &cbytes, (size_t)tiles_n * sizeof(unsigned), true);
+            if (st != LITELINEAR_OK) return st;
+            h->n_counters = cbytes / sizeof(unsigned);
+            p.partials = h->partials;
+            p.counters = h->counters;
+        }
+        return timed_launch(h, LITELINEAR_KERNEL_SKINNY, stream, [&] { return ll::launch_skinny(p, stream); });
+    }
+
+    ll::TiledProblem p{};
+    p.x = x;
+    p.A = A;
+    p.B = B;
+    p.Q = Q;
+    p.bias = bias;
+    p.y = y;
+    p.scale = scale;
+    p.M = M;
+    p.K = in;
+    p.N = out;
+    p.r = r;
+    p.r_pad = r_pad;
+    p.out_f32 = out_f32;
+    if (r > 0) {
+        st = grow(&h->t_ws, &h->t_ws_bytes, (size_t)M * r_pad * 2, false);
+        if (st != LITELINEAR_OK) return st;
+        p.t_ws = h->t_ws;
+        const ll::TileCfg pc = ll::choose_proj_tile(p);
+        st = timed_launch(h, LITELINEAR_KERNEL_LOWRANK_PROJ, stream, [&] { return ll::launch_proj(p, pc, stream); });
+        if (st != LITELINEAR_OK) return st;
+    }
+    const ll::TileCfg mc = ll::choose_main_tile(p);
+    return timed_launch(h, LITELINEAR_KERNEL_MAIN, stream, [&] { return ll::launch_main(p, mc, stream); });
+}
+
+}  // extern "C"

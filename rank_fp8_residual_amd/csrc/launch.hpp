@@ -1,0 +1,52 @@
+// Internal launch interface between the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ll {
+
+// Tiled path: T = x B^T into a bf16 workspace [M, r_pad], then the fused
+// kernel y = scale * x dec(Q)^T + T A^T + bias.
+struct TiledProblem {
+    const void *x, *A, *B, *Q, *bias;
+    void *y;
+    void *t_ws;          // bf16 [M, r_pad]; unused when r == 0
+    float scale;
+    int64_t M, K, N, r, r_pad;
+    bool out_f32;
+};
+
+// Tile configuration of one launch (work-group tile BM x BN).
+struct TileCfg {
+    int bm, bn;
+};
+
+// True when the tiled path divides T by scale before rounding it, so that
+// scale is applied in the fused kernel's epilogue (see tiled.hip).
+bool scale_foldable(float scale);
+TileCfg choose_proj_tile(const TiledProblem &p);
+TileCfg choose_main_tile(const TiledProblem &p);
+hipError_t launch_proj(const TiledProblem &p, TileCfg c, hipStream_t s);
+hipError_t launch_main(const TiledProblem &p, TileCfg c, hipStream_t s);
+
+// Skinny path: split-K over `in`; every work-group computes its own slice of
+// T, and the last work-group of each column tile sums the slices in order.
+struct SkinnyProblem {
+    const void *x, *A, *B, *Q, *bias;
+    void *y;
+    float *partials;     // float32 [splits, M, N] (used when splits > 1)
+    unsigned *counters;  // one per column tile, zero between calls
+    float scale;
+    int64_t M, K, N, r, r_pad;
+    int splits;          // number of K slices
+    int64_t k_slice;     // elements of K per slice (multiple of 64)
+    bool out_f32;
+};
+
+int skinny_col_tile();                        // columns per work-group
+bool skinny_supports(int64_t M, int64_t r_pad);  // shapes the skinny kernel takes
+int choose_skinny_splits(int64_t M, int64_t K, int64_t N);
+hipError_t launch_skinny(const SkinnyProblem &p, hipStream_t s);
+
+}  // namespace ll

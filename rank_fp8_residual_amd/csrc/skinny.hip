@@ -1,0 +1,360 @@
+// Skinny-M (HBM-bound) path of the fused LiteLinear forward on gfx950.
+//
+// The forward (LiteLinear README, page "moonmath-ai/LiteLinear", equation in
+// the introduction):  y = (x B^T) A^T + scale * (x dec(Q)^T) + bias.
+//
+// With few rows the time is the time to stream Q (out * in bytes) from HBM
+// once.  The reduction over `in` is split into slices so that enough
+// work-groups run to keep every CU loading; the grid is
+// (column tiles of 256 outputs) x (K slices).  A work-group:
+//   * streams its 256 x k_slice block of Q codes with 128-bit loads straight
+//     into registers (16 codes per lane per fragment), converts them exactly
+//     to bf16 and feeds v_mfma_f32_16x16x32_bf16 against the x rows;
+//   * computes its slice's share of T = x B^T on the same x registers
+//     (T = sum over slices of T_slice, so (sum T_slice) A^T = sum T_slice A^T
+//     and no separate pass over x is needed);
+//   * forms scale * acc + T_slice A^T, with T_slice rounded once to bf16;
+//   * writes that partial sum as float32; the last work-group of the column
+//     tile to finish (an atomic counter) adds the slices in slice order, adds
+//     bias and stores y.  The result does not depend on which work-group
+//     finishes last, and the counter is left at zero for the next call.
+// With one slice the partial step is skipped and y is stored directly.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace ll {
+namespace {
+
+constexpr int SNT = 256;            // threads per work-group (4 waves)
+constexpr int WNF = 4;              // 16-column fragments per wave
+constexpr int SBN = 4 * WNF * 16;   // output columns per work-group
+constexpr int SMAX_M = 64;          // largest M (4 row blocks of 16)
+
+struct SArgs {
+    const unsigned char *x, *B, *Q, *A, *bias;
+    void *y;
+    float *partials;
+    unsigned *counters;
+    float scale;
+    int64_t M, K, N, r, r_pad, k_slice;
+    int splits;
+    bool a_vec, y_vec;
+};
+
+// Operands of one 64-wide step of the reduction, as this lane holds them:
+// lane l covers reduction elements [k + 16*(l/16), +16) of row (l % 16) of
+// each 16-row fragment; both halves of 8 feed one matrix-core product each.
+template <int MB, int RT>
+struct Step {
+    u32x4 q[WNF];              // 16 e4m3fn codes per Q fragment
+    u32x4 x0[MB], x1[MB];      // 2 x 8 bf16 of x per row block
+    u32x4 b0[RT], b1[RT];      // 2 x 8 bf16 of B per rank fragment
+};
+
+template <int MB, int RT>
+__device__ __forceinline__ void load_step(Step<MB, RT> &st, const SArgs &a, int64_t k, int64_t ke,
+                                          int64_t nw, int wave, int lane) {
+    const int l16 = lane & 15;
+    const int64_t kl = k + 16 * (lane >> 4);
+    const bool kin = kl < ke;  // in % 16 == 0: a 16-element chunk is all in or all out
+#pragma unroll
+    for (int f = 0; f < WNF; ++f) {
+        const int64_t n = nw + f * 16 + l16;
+        st.q[f] = (kin && n < a.N) ? load16(a.Q + n * a.K + kl) : zero4();
+    }
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+        const int64_t m = b * 16 + l16;
+        if (kin && m < a.M) {
+            const unsigned char *p = a.x + (m * a.K + kl) * 2;
+            st.x0[b] = load16(p);
+            st.x1[b] = load16(p + 16);
+        } else {
+            st.x0[b] = zero4();
+            st.x1[b] = zero4();
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int64_t rr = (int64_t)(wave + 4 * t) * 16 + l16;
+        if (kin && rr < a.r) {
+            const unsigned char *p = a.B + (rr * a.K + kl) * 2;
+            st.b0[t] = load16(p);
+            st.b1[t] = load16(p + 16);
+        } else {
+            st.b0[t] = zero4();
+            st.b1[t] = zero4();
+        }
+    }
+}
+
+template <int MB, int RT>
+__device__ __forceinline__ void compute_step(const Step<MB, RT> &st, f32x4 (&acc)[WNF][MB],
+                                             f32x4 (&tacc)[RT][MB]) {
+#pragma unroll
+    for (int f = 0; f < WNF; ++f) {
+        u32x4 h0, h1;
+        fp8x16_to_bf16x16(st.q[f], h0, h1);
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+            acc[f][b] = mfma16(h0, st.x0[b], acc[f][b]);
+            acc[f][b] = mfma16(h1, st.x1[b], acc[f][b]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+            tacc[t][b] = mfma16(st.b0[t], st.x0[b], tacc[t][b]);
+            tacc[t][b] = mfma16(st.b1[t], st.x1[b], tacc[t][b]);
+        }
+}
+
+template <bool OUT_F32>
+__device__ __forceinline__ void store_out(const SArgs &a, int64_t m, int64_t n, const float (&o)[4]) {
+    if (OUT_F32) {
+        float *dst = reinterpret_cast<float *>(a.y) + m * a.N + n;
+        if (a.y_vec && n + 3 < a.N) {
+            *reinterpret_cast<f32x4 *>(dst) = f32x4{o[0], o[1], o[2], o[3]};
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (n + v < a.N) dst[v] = o[v];
+        }
+    } else {
+        unsigned short *dst = reinterpret_cast<unsigned short *>(a.y) + m * a.N + n;
+        if (a.y_vec && n + 3 < a.N) {
+            *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (n + v < a.N) dst[v] = f32_to_bf16_rne(o[v]);
+        }
+    }
+}
+
+template <int MB, int RT, bool OUT_F32>
+__global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
+    constexpr int TS_LD = RT * 64 + 8;  // bf16 per LDS row of the T slice (16-byte multiple)
+    __shared__ __attribute__((aligned(16))) unsigned short ts[MB * 16][TS_LD];
+    __shared__ unsigned is_last;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int tn = blockIdx.x, slice = blockIdx.y;
+    const int64_t nw = (int64_t)tn * SBN + wave * (WNF * 16);
+    const int64_t kb = (int64_t)slice * a.k_slice;
+    const int64_t ke = (kb + a.k_slice < a.K) ? kb + a.k_slice : a.K;
+
+    f32x4 acc[WNF][MB], tacc[RT][MB];
+#pragma unroll
+    for (int f = 0; f < WNF; ++f)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) tacc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Reduction over this slice, loads for step k+64 in flight during step k.
+    Step<MB, RT> s0, s1;
+    if (kb < ke) load_step(s0, a, kb, ke, nw, wave, lane);
+    for (int64_t k = kb; k < ke; k += 128) {
+        if (k + 64 < ke) load_step(s1, a, k + 64, ke, nw, wave, lane);
+        compute_step(s0, acc, tacc);
+        if (k + 64 >= ke) break;
+        if (k + 128 < ke) load_step(s0, a, k + 128, ke, nw, wave, lane);
+        compute_step(s1, acc, tacc);
+    }
+
+    // T slice -> LDS as bf16: lane holds T[m = 16b + l16][16 rf + 4g + v].
+    const int rfr = (int)(a.r_pad / 16);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const int rf = wave + 4 * t;
+        if (rf < rfr) {
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+                *reinterpret_cast<u32x2 *>(&ts[b * 16 + l16][rf * 16 + 4 * g]) =
+                    u32x2{pack_bf16x2(tacc[t][b][0], tacc[t][b][1]), pack_bf16x2(tacc[t][b][2], tacc[t][b][3])};
+        }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int f = 0; f < WNF; ++f)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[f][b] *= a.scale;
+
+    // acc += T_slice A^T over the padded rank (A is read as zero past r).
+    for (int64_t k2 = 0; k2 < a.r_pad; k2 += 32) {
+        const int64_t ka = k2 + 8 * g;
+        u32x4 bt[MB];
+#pragma unroll
+        for (int b = 0; b < MB; ++b) bt[b] = *reinterpret_cast<const u32x4 *>(&ts[b * 16 + l16][ka]);
+#pragma unroll
+        for (int f = 0; f < WNF; ++f) {
+            const int64_t n = nw + f * 16 + l16;
+            u32x4 av = zero4();
+            if (n < a.N && ka < a.r) {
+                const unsigned char *p = a.A + (n * a.r + ka) * 2;
+                if (a.a_vec) {
+                    av = load16(p);
+                } else {
+                    unsigned short e[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        e[t] = (ka + t < a.r) ? reinterpret_cast<const unsigned short *>(p)[t] : 0;
+                    av = u32x4{e[0] | (unsigned)e[1] << 16, e[2] | (unsigned)e[3] << 16,
+                               e[4] | (unsigned)e[5] << 16, e[6] | (unsigned)e[7] << 16};
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < MB; ++b) acc[f][b] = mfma16(av, bt[b], acc[f][b]);
+        }
+    }
+
+    // Lane holds acc[f][b][v] = y[m = 16b + l16][n = nw + 16f + 4g + v] (minus bias).
+    if (a.splits > 1) {
+#pragma unroll
+        for (int f = 0; f < WNF; ++f) {
+            const int64_t n = nw + f * 16 + 4 * g;
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+                const int64_t m = b * 16 + l16;
+                if (m >= a.M) continue;
+                float *dst = a.partials + ((int64_t)slice * a.M + m) * a.N + n;
+                if (a.y_vec && n + 3 < a.N) {
+                    *reinterpret_cast<f32x4 *>(dst) = acc[f][b];
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (n + v < a.N) dst[v] = acc[f][b][v];
+                }
+            }
+        }
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) {
+            const unsigned prev = atomicAdd(&a.counters[tn], 1u);
+            __threadfence();
+            is_last = (prev == (unsigned)(a.splits - 1)) ? 1u : 0u;
+        }
+        __syncthreads();
+        if (!is_last) return;
+        __threadfence();
+    }
+
+#pragma unroll
+    for (int f = 0; f < WNF; ++f) {
+        const int64_t n = nw + f * 16 + 4 * g;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (a.bias) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (n + v < a.N) bv[v] = bf16_to_f32(reinterpret_cast<const unsigned short *>(a.bias)[n + v]);
+        }
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+            const int64_t m = b * 16 + l16;
+            if (m >= a.M) continue;
+            float s[4] = {0.f, 0.f, 0.f, 0.f};
+            if (a.splits > 1) {
+                for (int sl = 0; sl < a.splits; ++sl) {
+                    const float *src = a.partials + ((int64_t)sl * a.M + m) * a.N + n;
+                    if (a.y_vec && n + 3 < a.N) {
+                        const f32x4 p = *reinterpret_cast<const f32x4 *>(src);
+                        s[0] += p[0];
+                        s[1] += p[1];
+                        s[2] += p[2];
+                        s[3] += p[3];
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            if (n + v < a.N) s[v] += src[v];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) s[v] = acc[f][b][v];
+            }
+            const float o[4] = {s[0] + bv[0], s[1] + bv[1], s[2] + bv[2], s[3] + bv[3]};
+            store_out<OUT_F32>(a, m, n, o);
+        }
+    }
+    if (a.splits > 1 && tid == 0) a.counters[tn] = 0u;
+}
+
+template <int MB, int RT, bool OUT_F32>
+hipError_t launch_sk(const SArgs &a, int tiles_n, hipStream_t s) {
+    hipLaunchKernelGGL((skinny_kernel<MB, RT, OUT_F32>), dim3(tiles_n, a.splits), dim3(SNT), 0, s, a);
+    return hipGetLastError();
+}
+
+// Row blocks (MB) x rank fragments per wave (RT) that are instantiated: the
+// register budget allows RT <= 8 / MB (larger combinations would spill).
+template <bool OUT_F32>
+hipError_t launch_sk_m(const SArgs &a, int tiles_n, hipStream_t s) {
+    const int64_t rt = (a.r_pad + 63) / 64;
+    if (a.M <= 16) {
+        if (rt <= 1) return launch_sk<1, 1, OUT_F32>(a, tiles_n, s);
+        if (rt <= 2) return launch_sk<1, 2, OUT_F32>(a, tiles_n, s);
+        if (rt <= 4) return launch_sk<1, 4, OUT_F32>(a, tiles_n, s);
+        if (rt <= 8) return launch_sk<1, 8, OUT_F32>(a, tiles_n, s);
+    } else if (a.M <= 32) {
+        if (rt <= 1) return launch_sk<2, 1, OUT_F32>(a, tiles_n, s);
+        if (rt <= 2) return launch_sk<2, 2, OUT_F32>(a, tiles_n, s);
+        if (rt <= 4) return launch_sk<2, 4, OUT_F32>(a, tiles_n, s);
+    } else if (a.M <= SMAX_M) {
+        if (rt <= 1) return launch_sk<4, 1, OUT_F32>(a, tiles_n, s);
+        if (rt <= 2) return launch_sk<4, 2, OUT_F32>(a, tiles_n, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int skinny_col_tile() { return SBN; }
+
+bool skinny_supports(int64_t M, int64_t r_pad) {
+    const int64_t rt = (r_pad + 63) / 64;
+    if (M <= 16) return rt <= 8;
+    if (M <= 32) return rt <= 4;
+    if (M <= SMAX_M) return rt <= 2;
+    return false;
+}
+
+int choose_skinny_splits(int64_t M, int64_t K, int64_t N) {
+    (void)M;
+    const int64_t tiles_n = (N + SBN - 1) / SBN;
+    const int64_t ksteps = (K + 63) / 64;
+    int64_t s = (256 + tiles_n - 1) / tiles_n;  // about one work-group per CU
+    if (s > ksteps / 4) s = ksteps / 4;         // keep >= 4 steps of 64 per slice
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+hipError_t launch_skinny(const SkinnyProblem &p, hipStream_t s) {
+    SArgs a{};
+    a.x = (const unsigned char *)p.x;
+    a.B = (const unsigned char *)p.B;
+    a.Q = (const unsigned char *)p.Q;
+    a.A = (const unsigned char *)p.A;
+    a.bias = (const unsigned char *)p.bias;
+    a.y = p.y;
+    a.partials = p.partials;
+    a.counters = p.counters;
+    a.scale = p.scale;
+    a.M = p.M;
+    a.K = p.K;
+    a.N = p.N;
+    a.r = p.r;
+    a.r_pad = p.r_pad;
+    a.k_slice = p.k_slice;
+    a.splits = p.splits;
+    a.a_vec = (p.r % 8 == 0) && ((uintptr_t)p.A % 16 == 0);
+    a.y_vec = (p.N % 4 == 0) && ((uintptr_t)p.y % 16 == 0) && ((uintptr_t)p.partials % 16 == 0);
+    const int tiles_n = (int)((p.N + SBN - 1) / SBN);
+    return p.out_f32 ? launch_sk_m<true>(a, tiles_n, s) : launch_sk_m<false>(a, tiles_n, s);
+}
+
+}  // namespace ll

@@ -1,0 +1,216 @@
+"""Thin ctypes binding of liblitelinear.so (see include/litelinear.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity and handed over as device pointers with torch's current HIP
+stream.  Every step of the forward runs in the library's HIP kernels; there
+is no other implementation to fall back to, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import enum
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblitelinear.so")
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+class Status(enum.IntEnum):
+    OK = 0
+    INVALID_ARG = 1
+    UNSUPPORTED = 2
+    HIP = 3
+    OOM = 4
+
+
+class Option(enum.IntEnum):
+    PATH = 1
+    OUTPUT_F32 = 2
+    SPLIT_K = 3
+    PROFILE = 4
+
+
+class Path(enum.IntEnum):
+    AUTO = 0
+    SKINNY = 1
+    TILED = 2
+
+
+class Kernel(enum.IntEnum):
+    LOWRANK_PROJ = 0
+    MAIN = 1
+    SKINNY = 2
+
+
+EXPORTS = ("litelinear_create", "litelinear_forward", "litelinear_destroy", "litelinear_check_args",
+           "litelinear_set_option", "litelinear_kernel_time", "litelinear_status_string",
+           "litelinear_version")
+
+
+class LiteLinearError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = Status(status) if status in Status._value2member_map_ else status
+        super().__init__(f"{what}: {lib().litelinear_status_string(status).decode()} (status {status})")
+
+
+def lib(path: str | None = None) -> ctypes.CDLL:
+    """Load the HIP library; raises ImportError when it has not been built."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"liblitelinear.so not found at {p}; build it with "
+                          "`python -m rank_fp8_residual_amd.build`")
+    with _lib_lock:
+        L = ctypes.CDLL(p)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.litelinear_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int]
+        L.litelinear_create.restype = ctypes.c_int
+        L.litelinear_destroy.argtypes = [vp]
+        L.litelinear_destroy.restype = ctypes.c_int
+        L.litelinear_forward.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, i64, i64, i64, i64, vp]
+        L.litelinear_forward.restype = ctypes.c_int
+        L.litelinear_check_args.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int]
+        L.litelinear_check_args.restype = ctypes.c_int
+        L.litelinear_set_option.argtypes = [vp, ctypes.c_int, i64]
+        L.litelinear_set_option.restype = ctypes.c_int
+        L.litelinear_kernel_time.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                             ctypes.POINTER(i64), ctypes.c_int]
+        L.litelinear_kernel_time.restype = ctypes.c_int
+        L.litelinear_status_string.argtypes = [ctypes.c_int]
+        L.litelinear_status_string.restype = ctypes.c_char_p
+        L.litelinear_version.argtypes = []
+        L.litelinear_version.restype = ctypes.c_char_p
+        if path is None:
+            _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != Status.OK:
+        raise LiteLinearError(status, what)
+
+
+def check_args(x, A, B, Q, bias, y, M, in_features, out_features, r, y_bytes_per_elem=2) -> Status:
+    """Host-only argument validation on raw integer addresses (no device use)."""
+    return Status(lib().litelinear_check_args(x, A, B, Q, bias, y, M, in_features, out_features, r,
+                                              y_bytes_per_elem))
+
+
+class Handle:
+    """Owns one litelinear handle (and its workspace) on one HIP device."""
+
+    def __init__(self, device: int | torch.device | None = None):
+        if device is None:
+            device = torch.cuda.current_device()
+        self.device = torch.device("cuda", device) if isinstance(device, int) else torch.device(device)
+        self._h = ctypes.c_void_p()
+        _check(lib().litelinear_create(ctypes.byref(self._h), self.device.index or 0), "litelinear_create")
+        self.out_f32 = False
+
+    def close(self):
+        if self._h:
+            _check(lib().litelinear_destroy(self._h), "litelinear_destroy")
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            if self._h:
+                lib().litelinear_destroy(self._h)
+        except Exception:
+            pass
+
+    def set_option(self, key: Option | int, value: int):
+        _check(lib().litelinear_set_option(self._h, int(key), int(value)), f"set_option({key})")
+        if int(key) == Option.OUTPUT_F32:
+            self.out_f32 = bool(value)
+
+    def kernel_time(self, kind: Kernel | int, reset: bool = False):
+        """(total milliseconds, launches) recorded for one kernel kind."""
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        _check(lib().litelinear_kernel_time(self._h, int(kind), ctypes.byref(ms), ctypes.byref(n), int(reset)),
+               "kernel_time")
+        return ms.value, n.value
+
+    def forward(self, x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, Q: torch.Tensor,
+                scale: float, bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+        """y = (x B^T) A^T + scale * (x dec(Q)^T) + bias on this handle's device."""
+        dev = self.device
+        if Q.dtype == torch.float8_e4m3fn:
+            Q = Q.view(torch.uint8)
+        _expect(Q, "Q", torch.uint8, dev, 2)
+        out_features, in_features = Q.shape
+        _expect(x, "x", torch.bfloat16, dev, None)
+        if x.shape[-1] != in_features:
+            raise ValueError(f"x has {x.shape[-1]} features, Q has {in_features}")
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, in_features)
+        if not x2.is_contiguous():
+            raise ValueError("x must be contiguous")
+        M = x2.shape[0]
+        if A is None or B is None:
+            if (A is None) != (B is None):
+                raise ValueError("A and B must both be given or both be None")
+            r = 0
+        else:
+            _expect(A, "A", torch.bfloat16, dev, 2)
+            _expect(B, "B", torch.bfloat16, dev, 2)
+            r = A.shape[1]
+            if A.shape[0] != out_features or B.shape != (r, in_features):
+                raise ValueError(f"A {tuple(A.shape)} / B {tuple(B.shape)} do not match "
+                                 f"out={out_features}, in={in_features}")
+        if bias is not None:
+            _expect(bias, "bias", torch.bfloat16, dev, 1)
+            if bias.shape[0] != out_features:
+                raise ValueError("bias must have out_features elements")
+        ydt = torch.float32 if self.out_f32 else torch.bfloat16
+        if out is None:
+            out = torch.empty((M, out_features), dtype=ydt, device=dev)
+        else:
+            _expect(out, "out", ydt, dev, None)
+            if out.numel() != M * out_features:
+                raise ValueError("out has the wrong number of elements")
+        s = (stream or torch.cuda.current_stream(dev)).cuda_stream
+        ptr = lambda t: None if t is None or t.numel() == 0 else t.data_ptr()
+        st = lib().litelinear_forward(self._h, ptr(x2), ptr(A) if r else None, ptr(B) if r else None, ptr(Q),
+                                      ctypes.c_float(float(scale)), ptr(bias), ptr(out), M, in_features,
+                                      out_features, r, s)
+        _check(st, "litelinear_forward")
+        return out.view(*lead, out_features)
+
+
+def _expect(t, name, dtype, dev, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, the handle on {dev}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_default_handles: dict[int, Handle] = {}
+
+
+def default_handle(device: int | None = None) -> Handle:
+    idx = torch.cuda.current_device() if device is None else device
+    h = _default_handles.get(idx)
+    if h is None:
+        h = _default_handles[idx] = Handle(idx)
+    return h
+
+
+def forward(x, A, B, Q, scale, bias=None, out=None):
+    """Functional form on the default handle of x's device."""
+    return default_handle(x.device.index).forward(x, A, B, Q, scale, bias, out)

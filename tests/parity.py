@@ -1,0 +1,67 @@
+"""Parity gates shared by the GPU tests and the bench.
+
+Tolerance (stated for the bf16 forward; the pages fix none):
+  * mean relative error, read as relative L1:  sum|y - y_ref| / sum|y_ref| <= 5e-3
+    (a per-element mean of |dy|/|y_ref| has no finite expectation when y_ref
+    has a density at zero, so it is reported only);
+  * max error against the float64 oracle:
+      - float32 output:  max|y - y_ref| <= 2e-2 * RMS(y_ref)        (literal)
+      - bf16 output:     |y - y_ref| <= 2e-2 * RMS(y_ref) + ulp_bf16(y_ref)/2
+        element-wise; the half-ulp is the rounding of the exact value to the
+        nearest bf16, which alone exceeds 2e-2 * RMS on the DiT workloads
+        (outlier channels put |y| up to ~7 RMS).
+The literal max/RMS figure is reported in every case.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+REL_L1_GATE = 5e-3
+MAX_RMS_GATE = 2e-2
+
+
+def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
+    """Half the bf16 spacing at |v| (8 significant bits)."""
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -126.0)
+    return np.where(a > 0, np.ldexp(1.0, (e - 8).astype(np.int64)), np.ldexp(1.0, -134))
+
+
+def to_f64(y: torch.Tensor) -> np.ndarray:
+    return y.detach().to("cpu").to(torch.float64).numpy()
+
+
+def bf16_of(v: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even of float64 values to bf16, back in float64."""
+    return torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def metrics(y: np.ndarray, y_ref: np.ndarray) -> dict:
+    d = np.abs(y - y_ref)
+    rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
+    l1 = float(np.sum(np.abs(y_ref)))
+    nz = np.abs(y_ref) > 0
+    return {
+        "rms": rms,
+        "max_abs": float(d.max()) if d.size else 0.0,
+        "max_over_rms": float(d.max() / rms) if d.size and rms > 0 else 0.0,
+        "rel_l1": float(d.sum() / l1) if l1 > 0 else float(d.sum()),
+        "mean_rel_elem": float(np.mean(d[nz] / np.abs(y_ref[nz]))) if nz.any() else 0.0,
+        "finite": bool(np.all(np.isfinite(y))),
+    }
+
+
+def check(y: np.ndarray, y_ref: np.ndarray, out_f32: bool, rms: float | None = None) -> dict:
+    """Assert the gates; ``rms`` overrides RMS(y_ref) (e.g. from a row sample)."""
+    m = metrics(y, y_ref)
+    r = m["rms"] if rms is None else rms
+    assert m["finite"], "non-finite output"
+    assert m["rel_l1"] <= REL_L1_GATE, m
+    bound = MAX_RMS_GATE * r
+    if not out_f32:
+        bound = bound + half_ulp_bf16(y_ref)
+    bad = np.abs(y - y_ref) > bound
+    assert not bad.any(), {**m, "n_bad": int(bad.sum()), "first_bad": np.argwhere(bad)[:3].tolist()}
+    return m

@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path through the C ABI against the float64 CPU oracle.
+
+Every case prints its name, shape, path and seed before it touches the GPU.
+Gates are in tests/parity.py.  Exact-arithmetic inputs must agree bit for
+bit; the e4m3fn decode must be bit-exact for every code.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rank_fp8_residual_amd import Handle, Kernel, LiteLinearError, Option, Path, Status
+from rank_fp8_residual_amd import workloads as wl
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def to_dev(d, dev):
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    return g
+
+
+def make_handle(dev, path=Path.AUTO, out_f32=False, split=0):
+    h = Handle(dev.index)
+    h.set_option(Option.PATH, int(path))
+    h.set_option(Option.OUTPUT_F32, int(out_f32))
+    h.set_option(Option.SPLIT_K, split)
+    return h
+
+
+def run(h, g):
+    y = h.forward(g["x"], g["A"] if g["r"] else None, g["B"] if g["r"] else None, g["Q"], g["scale"], g["bias"])
+    torch.cuda.synchronize()
+    return y
+
+
+def oracle_y(d, rows=None):
+    return oracle.forward(d["x"], d["A"] if d["r"] else None, d["B"] if d["r"] else None, d["Q"],
+                          d["scale"], d["bias"], rows=rows)
+
+
+PATHS = [Path.SKINNY, Path.TILED]
+
+
+# ------------------------------------------------------------ exact decode
+
+@pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
+def test_decode_every_code_bit_exact(dev, path):
+    """y = x dec(Q)^T with x = identity returns every e4m3fn value exactly."""
+    say("decode", path.name)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    K = 256
+    Qn = np.zeros((16, K), np.uint8)
+    for i in range(16):
+        Qn[i] = np.roll(np.concatenate([codes, codes[:2]]), 17 * i)[:K]
+    d = {"x": torch.eye(K, dtype=torch.bfloat16)[:64].contiguous(), "A": None, "B": None,
+         "Q": torch.from_numpy(Qn), "scale": 1.0, "bias": None, "M": 64, "in": K, "out": 16, "r": 0}
+    h = make_handle(dev, path, out_f32=True)
+    y = parity.to_f64(run(h, to_dev(d, dev)))
+    expect = oracle.decode_e4m3fn(Qn[:, :64]).T
+    assert np.array_equal(y, expect)
+    assert np.array_equal(np.signbit(y), np.signbit(expect))
+
+
+# ------------------------------------------------------- exact arithmetic
+
+EXACT_SHAPES = [  # M, in, out, r
+    (1, 16, 5, 0), (7, 48, 17, 3), (16, 64, 256, 16), (33, 320, 200, 17), (64, 256, 260, 64),
+    (67, 96, 129, 1), (130, 64, 300, 100), (257, 512, 513, 64), (300, 2048, 64, 128),
+]
+
+
+@pytest.mark.parametrize("shape", EXACT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("out_f32", [False, True], ids=["bf16", "f32"])
+def test_exact_inputs_bitwise(dev, shape, out_f32):
+    M, K, N, r = shape
+    d = wl.exact_inputs(M, K, N, r, seed=M + K + N + r)
+    y_ref = oracle_y(d)
+    expect = y_ref if out_f32 else parity.bf16_of(y_ref)
+    g = to_dev(d, dev)
+    for path in PATHS:
+        if path == Path.SKINNY and M > 64:
+            continue
+        say("exact", shape, path.name, "f32" if out_f32 else "bf16")
+        y = parity.to_f64(run(make_handle(dev, path, out_f32), g))
+        bad = np.argwhere(y != expect)
+        assert bad.size == 0, (path.name, bad[:5].tolist(), y[tuple(bad[0])], expect[tuple(bad[0])])
+
+
+# --------------------------------------------------- random small shapes
+
+RANDOM_SHAPES = [  # M, in, out, r: several tiles and ragged tails
+    (1, 256, 300, 16), (16, 1024, 777, 64), (40, 512, 512, 32), (64, 2048, 1024, 64),
+    (65, 256, 256, 16), (200, 1024, 520, 48), (513, 512, 700, 64), (1000, 768, 1030, 256),
+]
+
+
+@pytest.mark.parametrize("shape", RANDOM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("out_f32", [False, True], ids=["bf16", "f32"])
+def test_random_parity(dev, shape, out_f32):
+    M, K, N, r = shape
+    d = wl.random_inputs(M, K, N, r, seed=1000 + M)
+    y_ref = oracle_y(d)
+    g = to_dev(d, dev)
+    for path in PATHS:
+        if path == Path.SKINNY and M > 64:
+            continue
+        say("random", shape, path.name, "f32" if out_f32 else "bf16")
+        y = parity.to_f64(run(make_handle(dev, path, out_f32), g))
+        parity.check(y, y_ref, out_f32)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 32])
+def test_skinny_split_counts(dev, splits):
+    d = wl.random_inputs(16, 2048, 640, 64, seed=7)
+    y_ref = oracle_y(d)
+    say("skinny splits", splits)
+    h = make_handle(dev, Path.SKINNY, split=splits)
+    g = to_dev(d, dev)
+    y1 = run(h, g)
+    y2 = run(h, g)  # the counters must be back at zero for the second call
+    assert torch.equal(y1, y2)
+    parity.check(parity.to_f64(y1), y_ref, False)
+
+
+# ------------------------------------------------------ full workloads
+
+def sample_rows(M, n=48):
+    rows = np.unique(np.concatenate([np.linspace(0, M - 1, n).astype(np.int64), [0, M - 1, max(M - 7, 0)]]))
+    return rows
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_workload_parity(dev, name):
+    """Full-size workloads in the launch configuration the bench times (the
+    automatic path), checked on rows the oracle computes one by one."""
+    w = wl.WORKLOADS[name]
+    say("workload", name, w)
+    d = wl.make_inputs(w, seed=0)
+    g = to_dev(d, dev)
+    h = make_handle(dev, Path.AUTO)
+    y = run(h, g)
+    assert bool(torch.isfinite(y).all())
+    rows = np.arange(w.M) if w.M <= 64 else sample_rows(w.M)
+    y_ref = oracle_y(d, rows=rows)
+    ys = parity.to_f64(y[torch.from_numpy(rows).to(dev)])
+    m = parity.check(ys, y_ref, False)
+    say("workload", name, {k: round(v, 6) if isinstance(v, float) else v for k, v in m.items()})
+    # the float32-output mode must pass the literal max gate
+    h.set_option(Option.OUTPUT_F32, 1)
+    y32 = run(h, g)
+    parity.check(parity.to_f64(y32[torch.from_numpy(rows).to(dev)]), y_ref, True)
+    del g, y, y32
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------- edge cases
+
+def test_usage_example_shape(dev):
+    """README Usage: in=4096, out=16384, rank=64, x (8, 4096) -> y (8, 16384)."""
+    d = wl.random_inputs(8, 4096, 16384, 64, seed=3)
+    g = to_dev(d, dev)
+    say("usage example")
+    y = Handle(0).forward(g["x"], g["A"], g["B"], g["Q"], g["scale"], g["bias"])
+    torch.cuda.synchronize()
+    assert y.shape == (8, 16384) and y.dtype == torch.bfloat16
+    parity.check(parity.to_f64(y), oracle_y(d), False)
+
+
+def test_leading_dims_flatten(dev):
+    d = wl.random_inputs(24, 256, 96, 8, seed=4)
+    g = to_dev(d, dev)
+    say("leading dims")
+    y = Handle(0).forward(g["x"].view(2, 3, 4, 256), g["A"], g["B"], g["Q"], g["scale"], g["bias"])
+    torch.cuda.synchronize()
+    assert y.shape == (2, 3, 4, 96)
+    parity.check(parity.to_f64(y.reshape(24, 96)), oracle_y(d), False)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
+def test_degenerate_cases(dev, path):
+    h = make_handle(dev, path)
+    # r = 0: pure scaled residual; no bias
+    d = wl.random_inputs(12, 128, 72, 0, seed=5, with_bias=False)
+    say("r=0 no bias", path.name)
+    parity.check(parity.to_f64(run(h, to_dev(d, dev))), oracle_y(d), False)
+    # Q = 0: pure low-rank (the SVDLinearLayer forward)
+    d = wl.random_inputs(12, 128, 72, 16, seed=6)
+    d["Q"] = torch.zeros_like(d["Q"])
+    say("Q=0", path.name)
+    parity.check(parity.to_f64(run(h, to_dev(d, dev))), oracle_y(d), False)
+    # A = B = 0: pure scaled residual through the rank-r machinery
+    d = wl.random_inputs(12, 128, 72, 16, seed=7)
+    d["A"], d["B"] = torch.zeros_like(d["A"]), torch.zeros_like(d["B"])
+    say("A=B=0", path.name)
+    parity.check(parity.to_f64(run(h, to_dev(d, dev))), oracle_y(d), False)
+    # scale = 0 and an extreme scale (the tiled path's unfolded order)
+    for s in (0.0, 2.0 ** -70, 2.0 ** 70):
+        d = wl.random_inputs(12, 128, 72, 16, seed=8)
+        d["scale"] = s
+        say("scale", s, path.name)
+        parity.check(parity.to_f64(run(h, to_dev(d, dev))), oracle_y(d), False)
+
+
+def test_in_zero_gives_bias(dev):
+    say("in=0")
+    N = 40
+    bias = (torch.arange(N, dtype=torch.float32) / 8).to(torch.bfloat16).to(dev)
+    x = torch.empty((5, 0), dtype=torch.bfloat16, device=dev)
+    Q = torch.empty((N, 0), dtype=torch.uint8, device=dev)
+    A = torch.ones((N, 4), dtype=torch.bfloat16, device=dev)
+    B = torch.empty((4, 0), dtype=torch.bfloat16, device=dev)
+    y = Handle(0).forward(x, A, B, Q, 1.0, bias)
+    torch.cuda.synchronize()
+    assert torch.equal(y, bias.expand(5, N))
+
+
+def test_empty_m_is_a_noop(dev):
+    say("M=0")
+    d = wl.random_inputs(0, 64, 32, 4, seed=9)
+    g = to_dev(d, dev)
+    out = torch.full((0, 32), 7.0, dtype=torch.bfloat16, device=dev)
+    y = Handle(0).forward(g["x"], g["A"], g["B"], g["Q"], g["scale"], g["bias"], out=out)
+    assert y.shape == (0, 32)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
+def test_no_stores_outside_y(dev, path):
+    """Canary regions around y stay untouched (ragged M and out)."""
+    M, K, N, r = 37, 256, 203, 20
+    d = wl.random_inputs(M, K, N, r, seed=10)
+    g = to_dev(d, dev)
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), -77.0, dtype=torch.bfloat16, device=dev)
+    y = buf[pad:pad + M * N].view(M, N)
+    say("canary", path.name)
+    make_handle(dev, path).forward(g["x"], g["A"], g["B"], g["Q"], g["scale"], g["bias"], out=y)
+    torch.cuda.synchronize()
+    assert bool((buf[:pad] == -77.0).all()) and bool((buf[pad + M * N:] == -77.0).all())
+    parity.check(parity.to_f64(y), oracle_y(d), False)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
+def test_repeat_is_bitwise_deterministic(dev, path):
+    d = wl.random_inputs(48, 1024, 1000, 64, seed=11)
+    g = to_dev(d, dev)
+    h = make_handle(dev, path)
+    say("determinism", path.name)
+    assert torch.equal(run(h, g), run(h, g))
+
+
+def test_bad_arguments_return_status(dev):
+    d = wl.random_inputs(16, 64, 32, 4, seed=12)
+    g = to_dev(d, dev)
+    h = Handle(0)
+    say("bad args")
+    with pytest.raises(LiteLinearError) as e:  # misaligned x (offset by one element)
+        xs = torch.zeros(16 * 64 + 1, dtype=torch.bfloat16, device=dev)[1:].view(16, 64)
+        h.forward(xs, g["A"], g["B"], g["Q"], g["scale"], g["bias"])
+    assert e.value.status == Status.UNSUPPORTED
+    with pytest.raises(LiteLinearError) as e:  # y aliases x
+        h.forward(g["x"], g["A"], g["B"], g["Q"], g["scale"], g["bias"], out=g["x"].view(-1)[:16 * 32].view(16, 32))
+    assert e.value.status == Status.INVALID_ARG
+    h.set_option(Option.PATH, int(Path.SKINNY))
+    with pytest.raises(LiteLinearError) as e:  # the skinny kernel does not take M > 64
+        d2 = to_dev(wl.random_inputs(65, 64, 32, 4, seed=13), dev)
+        h.forward(d2["x"], d2["A"], d2["B"], d2["Q"], d2["scale"], d2["bias"])
+    assert e.value.status == Status.UNSUPPORTED
+
+
+def test_profiling_counts_launches(dev):
+    d = wl.random_inputs(128, 256, 256, 16, seed=14)
+    g = to_dev(d, dev)
+    h = make_handle(dev, Path.TILED)
+    h.set_option(Option.PROFILE, 1)
+    say("profile")
+    for _ in range(3):
+        run(h, g)
+    ms, n = h.kernel_time(Kernel.MAIN)
+    assert n == 3 and ms > 0
+    ms, n = h.kernel_time(Kernel.LOWRANK_PROJ, reset=True)
+    assert n == 3
+    assert h.kernel_time(Kernel.LOWRANK_PROJ) == (0.0, 0)
