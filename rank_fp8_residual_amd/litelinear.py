@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import enum
+import math
 import os
 import threading
 
@@ -152,7 +153,7 @@ class Handle:
         if x.shape[-1] != in_features:
             raise ValueError(f"x has {x.shape[-1]} features, Q has {in_features}")
         lead = x.shape[:-1]
-        x2 = x.reshape(-1, in_features)
+        x2 = x.reshape(math.prod(lead), in_features)
         if not x2.is_contiguous():
             raise ValueError("x must be contiguous")
         M = x2.shape[0]
