@@ -63,16 +63,20 @@ typedef enum {
 
 /* Kernels whose time litelinear_kernel_time() reports. */
 typedef enum {
-    LITELINEAR_KERNEL_LOWRANK_PROJ = 0, /* T = x B^T (tiled path) */
-    LITELINEAR_KERNEL_MAIN = 1,         /* the fused residual + rank-r + bias kernel (tiled path) */
-    LITELINEAR_KERNEL_SKINNY = 2        /* the skinny split-K kernel */
+    LITELINEAR_KERNEL_PAD_A = 0,  /* copy of A into a zero-padded [out, r_pad] buffer (tiled path,
+                                     only when r % 8 != 0 or A is not 16-byte aligned) */
+    LITELINEAR_KERNEL_MAIN = 1,   /* tiled path: T = x B^T, residual, rank-r product and bias */
+    LITELINEAR_KERNEL_SKINNY = 2  /* the skinny split-K kernel */
 } litelinear_kernel_t;
 
 /*
  * Create a handle bound to HIP device `device_ordinal`.  The handle owns the
- * workspace (the T = x B^T buffer of the tiled path, the split-K partial sums
- * and counters of the skinny path); it grows on demand inside
- * litelinear_forward.  One handle must not be used by two streams at once.
+ * workspace (the T = x B^T buffer and per-row-tile counters of the tiled
+ * path, a padded copy of A for ranks that are not a multiple of 8, the
+ * split-K partial sums and counters of the skinny path); it grows on demand
+ * inside litelinear_forward (hipMalloc, after synchronising the device).
+ * Calls on one handle must be ordered (one stream at a time): they share the
+ * workspace.
  * Errors: INVALID_ARG (out == NULL or no such device), HIP, OOM.
  */
 litelinear_status_t litelinear_create(litelinear_handle_t *out, int device_ordinal);

@@ -56,6 +56,10 @@ struct litelinear_ctx {
     int device = 0;
     void *t_ws = nullptr;
     size_t t_ws_bytes = 0;
+    unsigned *tile_sync = nullptr;  // tiled path: per-row-tile counters (flags, done)
+    size_t tile_sync_bytes = 0;
+    void *a_pad = nullptr;          // tiled path: zero-padded copy of A
+    size_t a_pad_bytes = 0;
     float *partials = nullptr;
     size_t partials_bytes = 0;
     unsigned *counters = nullptr;
@@ -181,6 +185,8 @@ litelinear_status_t litelinear_destroy(litelinear_handle_t h) {
         DeviceGuard g(h->device);
         if (hipDeviceSynchronize() != hipSuccess) st = LITELINEAR_ERR_HIP;
         if (h->t_ws) (void)hipFree(h->t_ws);
+        if (h->tile_sync) (void)hipFree(h->tile_sync);
+        if (h->a_pad) (void)hipFree(h->a_pad);
         if (h->partials) (void)hipFree(h->partials);
         if (h->counters) (void)hipFree(h->counters);
         for (auto &p : h->prof)
@@ -308,16 +314,29 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
     p.r = r;
     p.r_pad = r_pad;
     p.out_f32 = out_f32;
+    const ll::TileCfg mc = ll::choose_main_tile(p);
+    if (!ll::tiled_shape_ok(p, mc)) return LITELINEAR_ERR_UNSUPPORTED;
+    const void *a_eff = A;
+    unsigned *flags = nullptr, *done = nullptr;
     if (r > 0) {
         st = grow(&h->t_ws, &h->t_ws_bytes, (size_t)M * r_pad * 2, false);
         if (st != LITELINEAR_OK) return st;
         p.t_ws = h->t_ws;
-        const ll::TileCfg pc = ll::choose_proj_tile(p);
-        st = timed_launch(h, LITELINEAR_KERNEL_LOWRANK_PROJ, stream, [&] { return ll::launch_proj(p, pc, stream); });
+        const size_t tiles = (size_t)ll::tiled_row_tiles(p, mc);
+        st = grow((void **)&h->tile_sync, &h->tile_sync_bytes, 2 * tiles * sizeof(unsigned), true);
         if (st != LITELINEAR_OK) return st;
+        flags = h->tile_sync;
+        done = h->tile_sync + tiles;
+        if (ll::a_needs_padding(p)) {
+            st = grow(&h->a_pad, &h->a_pad_bytes, (size_t)out * r_pad * 2, false);
+            if (st != LITELINEAR_OK) return st;
+            st = timed_launch(h, LITELINEAR_KERNEL_PAD_A, stream, [&] { return ll::launch_pad_a(p, h->a_pad, stream); });
+            if (st != LITELINEAR_OK) return st;
+            a_eff = h->a_pad;
+        }
     }
-    const ll::TileCfg mc = ll::choose_main_tile(p);
-    return timed_launch(h, LITELINEAR_KERNEL_MAIN, stream, [&] { return ll::launch_main(p, mc, stream); });
+    return timed_launch(h, LITELINEAR_KERNEL_MAIN, stream,
+                        [&] { return ll::launch_tiled(p, mc, a_eff, flags, done, stream); });
 }
 
 }  // extern "C"

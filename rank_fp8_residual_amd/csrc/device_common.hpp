@@ -64,4 +64,38 @@ __device__ __forceinline__ u32x4 load16(const void *p) {
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
+// ---- buffer (descriptor-based) loads: an offset at or past the descriptor's
+// byte count reads as zero, so masking needs no branch.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr unsigned kOOB = 0x80000000u;  // an offset past every descriptor built here
+
+// Raw buffer over [base, base + bytes); bytes must stay below 2^31.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int n = bytes <= 0 ? 0 : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// 16 bytes per lane from the buffer straight into LDS: lane l's bytes land at
+// lds + 16 * l (lds is wave-uniform).  Counts against vmcnt like any load.
+__device__ __forceinline__ void bload16_lds(rsrc_t r, void *lds, unsigned off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, off, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, others left open).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Work-group barrier without a memory fence (loads may stay in flight).
+__device__ __forceinline__ void barrier_nofence() { __builtin_amdgcn_s_barrier(); }
+
 }  // namespace ll

@@ -6,8 +6,9 @@
 
 namespace ll {
 
-// Tiled path: T = x B^T into a bf16 workspace [M, r_pad], then the fused
-// kernel y = scale * x dec(Q)^T + T A^T + bias.
+// Tiled path: one launch whose first work-groups compute T' = x B^T / scale
+// into a bf16 workspace [M, r_pad] and whose other work-groups each produce
+// one output tile y = scale * (x dec(Q)^T + T' A^T) + bias.
 struct TiledProblem {
     const void *x, *A, *B, *Q, *bias;
     void *y;
@@ -23,12 +24,19 @@ struct TileCfg {
 };
 
 // True when the tiled path divides T by scale before rounding it, so that
-// scale is applied in the fused kernel's epilogue (see tiled.hip).
+// scale is applied in the epilogue (see tiled.hip).
 bool scale_foldable(float scale);
-TileCfg choose_proj_tile(const TiledProblem &p);
 TileCfg choose_main_tile(const TiledProblem &p);
-hipError_t launch_proj(const TiledProblem &p, TileCfg c, hipStream_t s);
-hipError_t launch_main(const TiledProblem &p, TileCfg c, hipStream_t s);
+// A's rows must be whole 16-byte chunks (r % 8 == 0, 16-byte aligned base);
+// otherwise it is first copied into a zero-padded [N, r_pad] workspace.
+bool a_needs_padding(const TiledProblem &p);
+bool tiled_shape_ok(const TiledProblem &p, TileCfg c);
+int tiled_row_tiles(const TiledProblem &p, TileCfg c);
+hipError_t launch_pad_a(const TiledProblem &p, void *a_pad, hipStream_t s);
+// flags / done: two arrays of tiled_row_tiles() counters, zero before the
+// launch and left at zero by it.
+hipError_t launch_tiled(const TiledProblem &p, TileCfg c, const void *a_eff, unsigned *flags, unsigned *done,
+                        hipStream_t s);
 
 // Skinny path: split-K over `in`; every work-group computes its own slice of
 // T, and the last work-group of each column tile sums the slices in order.

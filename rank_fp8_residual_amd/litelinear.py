@@ -44,7 +44,7 @@ class Path(enum.IntEnum):
 
 
 class Kernel(enum.IntEnum):
-    LOWRANK_PROJ = 0
+    PAD_A = 0
     MAIN = 1
     SKINNY = 2
 

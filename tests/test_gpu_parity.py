@@ -284,15 +284,17 @@ def test_bad_arguments_return_status(dev):
 
 
 def test_profiling_counts_launches(dev):
-    d = wl.random_inputs(128, 256, 256, 16, seed=14)
+    d = wl.random_inputs(128, 256, 256, 20, seed=14)   # r % 8 != 0: A is padded first
     g = to_dev(d, dev)
     h = make_handle(dev, Path.TILED)
     h.set_option(Option.PROFILE, 1)
     say("profile")
     for _ in range(3):
-        run(h, g)
+        y = run(h, g)
+    parity.check(parity.to_f64(y), oracle_y(d), False)
     ms, n = h.kernel_time(Kernel.MAIN)
     assert n == 3 and ms > 0
-    ms, n = h.kernel_time(Kernel.LOWRANK_PROJ, reset=True)
+    ms, n = h.kernel_time(Kernel.PAD_A, reset=True)
     assert n == 3
-    assert h.kernel_time(Kernel.LOWRANK_PROJ) == (0.0, 0)
+    assert h.kernel_time(Kernel.PAD_A) == (0.0, 0)
+    assert h.kernel_time(Kernel.SKINNY) == (0.0, 0)
