@@ -263,6 +263,18 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
     if (path == 0) path = (in > 0 && M <= kSkinnyAutoMaxM && ll::skinny_supports(M, r_pad)) ? 1 : 2;
     if (path == 1 && (in == 0 || !ll::skinny_supports(M, r_pad))) return LITELINEAR_ERR_UNSUPPORTED;
 
+    // A whose rows are not whole 16-byte chunks is first copied into a
+    // zero-padded [out, r_pad] buffer (both paths read A in 16-byte chunks).
+    const void *a_eff = A;
+    if (ll::a_needs_padding(r, A)) {
+        st = grow(&h->a_pad, &h->a_pad_bytes, (size_t)out * r_pad * 2, false);
+        if (st != LITELINEAR_OK) return st;
+        st = timed_launch(h, LITELINEAR_KERNEL_PAD_A, stream,
+                          [&] { return ll::launch_pad_a(A, h->a_pad, out, r, r_pad, stream); });
+        if (st != LITELINEAR_OK) return st;
+        a_eff = h->a_pad;
+    }
+
     if (path == 1) {
         const int64_t ksteps = cdiv(in, 64);
         int64_t splits = h->opt_split > 0 ? h->opt_split : ll::choose_skinny_splits(M, in, out);
@@ -270,6 +282,7 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
         if (splits < 1) splits = 1;
         const int64_t k_slice = cdiv(ksteps, splits) * 64;
         splits = cdiv(in, k_slice);
+        if (!ll::skinny_shape_ok(M, in, out, r_pad, splits)) return LITELINEAR_ERR_UNSUPPORTED;
         const int64_t tiles_n = cdiv(out, ll::skinny_col_tile());
         ll::SkinnyProblem p{};
         p.x = x;
@@ -297,7 +310,7 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
             p.partials = h->partials;
             p.counters = h->counters;
         }
-        return timed_launch(h, LITELINEAR_KERNEL_SKINNY, stream, [&] { return ll::launch_skinny(p, stream); });
+        return timed_launch(h, LITELINEAR_KERNEL_SKINNY, stream, [&] { return ll::launch_skinny(p, a_eff, stream); });
     }
 
     ll::TiledProblem p{};
@@ -316,7 +329,6 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
     p.out_f32 = out_f32;
     const ll::TileCfg mc = ll::choose_main_tile(p);
     if (!ll::tiled_shape_ok(p, mc)) return LITELINEAR_ERR_UNSUPPORTED;
-    const void *a_eff = A;
     unsigned *flags = nullptr, *done = nullptr;
     if (r > 0) {
         st = grow(&h->t_ws, &h->t_ws_bytes, (size_t)M * r_pad * 2, false);
@@ -327,13 +339,6 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
         if (st != LITELINEAR_OK) return st;
         flags = h->tile_sync;
         done = h->tile_sync + tiles;
-        if (ll::a_needs_padding(p)) {
-            st = grow(&h->a_pad, &h->a_pad_bytes, (size_t)out * r_pad * 2, false);
-            if (st != LITELINEAR_OK) return st;
-            st = timed_launch(h, LITELINEAR_KERNEL_PAD_A, stream, [&] { return ll::launch_pad_a(p, h->a_pad, stream); });
-            if (st != LITELINEAR_OK) return st;
-            a_eff = h->a_pad;
-        }
     }
     return timed_launch(h, LITELINEAR_KERNEL_MAIN, stream,
                         [&] { return ll::launch_tiled(p, mc, a_eff, flags, done, stream); });

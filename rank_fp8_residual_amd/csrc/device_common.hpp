@@ -77,14 +77,40 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
 }
 
+// Only whole 16-byte results are used from these loads: extracting single
+// elements of a buffer-load result has been seen to shrink the load wrongly.
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, unsigned off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// Cache policy of a load or store.  kDeviceCoherent (the sc1 bit) makes a
+// load read, and a store write, at device scope: it never returns a line
+// that another XCD's L2 has made stale, and a store is complete (vmcnt)
+// only once it is visible to every XCD.  Data handed between work-groups of
+// one launch travels this way, so no fence has to write back or invalidate
+// a whole L2.
+constexpr int kCached = 0;
+constexpr int kDeviceCoherent = 16;
+
 // 16 bytes per lane from the buffer straight into LDS: lane l's bytes land at
 // lds + 16 * l (lds is wave-uniform).  Counts against vmcnt like any load.
+template <int POLICY = kCached>
 __device__ __forceinline__ void bload16_lds(rsrc_t r, void *lds, unsigned off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, off, 0, 0, POLICY);
+}
+
+template <int POLICY>
+__device__ __forceinline__ void bstore8(rsrc_t r, unsigned off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, POLICY);
+}
+
+// Device-scope counter read without acquire side effects (no cache
+// invalidation), for polling.
+__device__ __forceinline__ unsigned poll_u32(const unsigned *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned bump_u32(unsigned *p) {
+    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight

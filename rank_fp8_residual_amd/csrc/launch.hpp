@@ -29,10 +29,10 @@ bool scale_foldable(float scale);
 TileCfg choose_main_tile(const TiledProblem &p);
 // A's rows must be whole 16-byte chunks (r % 8 == 0, 16-byte aligned base);
 // otherwise it is first copied into a zero-padded [N, r_pad] workspace.
-bool a_needs_padding(const TiledProblem &p);
+bool a_needs_padding(int64_t r, const void *A);
 bool tiled_shape_ok(const TiledProblem &p, TileCfg c);
 int tiled_row_tiles(const TiledProblem &p, TileCfg c);
-hipError_t launch_pad_a(const TiledProblem &p, void *a_pad, hipStream_t s);
+hipError_t launch_pad_a(const void *A, void *a_pad, int64_t N, int64_t r, int64_t r_pad, hipStream_t s);
 // flags / done: two arrays of tiled_row_tiles() counters, zero before the
 // launch and left at zero by it.
 hipError_t launch_tiled(const TiledProblem &p, TileCfg c, const void *a_eff, unsigned *flags, unsigned *done,
@@ -54,7 +54,9 @@ struct SkinnyProblem {
 
 int skinny_col_tile();                        // columns per work-group
 bool skinny_supports(int64_t M, int64_t r_pad);  // shapes the skinny kernel takes
+bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t splits);
 int choose_skinny_splits(int64_t M, int64_t K, int64_t N);
-hipError_t launch_skinny(const SkinnyProblem &p, hipStream_t s);
+// a_eff: A itself, or its zero-padded [N, r_pad] copy (see a_needs_padding).
+hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t s);
 
 }  // namespace ll

@@ -7,18 +7,22 @@
 // once.  The reduction over `in` is split into slices so that enough
 // work-groups run to keep every CU loading; the grid is
 // (column tiles of 256 outputs) x (K slices).  A work-group:
-//   * streams its 256 x k_slice block of Q codes with 128-bit loads straight
-//     into registers (16 codes per lane per fragment), converts them exactly
-//     to bf16 and feeds v_mfma_f32_16x16x32_bf16 against the x rows;
+//   * streams its 256 x k_slice block of Q codes with 128-bit buffer loads
+//     straight into registers (16 codes per lane per fragment), D steps of 64
+//     ahead, converts them exactly to bf16 and feeds
+//     v_mfma_f32_16x16x32_bf16 against the x rows;
 //   * computes its slice's share of T = x B^T on the same x registers
 //     (T = sum over slices of T_slice, so (sum T_slice) A^T = sum T_slice A^T
 //     and no separate pass over x is needed);
 //   * forms scale * acc + T_slice A^T, with T_slice rounded once to bf16;
-//   * writes that partial sum as float32; the last work-group of the column
-//     tile to finish (an atomic counter) adds the slices in slice order, adds
-//     bias and stores y.  The result does not depend on which work-group
-//     finishes last, and the counter is left at zero for the next call.
+//   * writes that partial sum as float32 with device-coherent stores; the
+//     last work-group of the column tile to finish (an atomic counter) reads
+//     the slices back with device-coherent loads, adds them in slice order,
+//     adds bias and stores y.  The result does not depend on which
+//     work-group finishes last, and the counter is left at zero.
 // With one slice the partial step is skipped and y is stored directly.
+// Every load is a buffer load: reads past a descriptor's end return zero,
+// so masking rows, columns and the K tail needs no branch.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -36,9 +40,8 @@ struct SArgs {
     float *partials;
     unsigned *counters;
     float scale;
-    int64_t M, K, N, r, r_pad, k_slice;
-    int splits;
-    bool a_vec, y_vec;
+    int M, K, N, r, r_pad, lda, k_slice, splits;
+    bool y_vec;
 };
 
 // Operands of one 64-wide step of the reduction, as this lane holds them:
@@ -51,40 +54,33 @@ struct Step {
     u32x4 b0[RT], b1[RT];      // 2 x 8 bf16 of B per rank fragment
 };
 
+struct Bufs {
+    rsrc_t q, x, b;
+};
+
 template <int MB, int RT>
-__device__ __forceinline__ void load_step(Step<MB, RT> &st, const SArgs &a, int64_t k, int64_t ke,
-                                          int64_t nw, int wave, int lane) {
+__device__ __forceinline__ void load_step(Step<MB, RT> &st, const Bufs &bf, const SArgs &a, int k, int ke,
+                                          int wave, int lane) {
     const int l16 = lane & 15;
-    const int64_t kl = k + 16 * (lane >> 4);
+    const int kl = k + 16 * (lane >> 4);
     const bool kin = kl < ke;  // in % 16 == 0: a 16-element chunk is all in or all out
 #pragma unroll
     for (int f = 0; f < WNF; ++f) {
-        const int64_t n = nw + f * 16 + l16;
-        st.q[f] = (kin && n < a.N) ? load16(a.Q + n * a.K + kl) : zero4();
+        const int row = wave * (WNF * 16) + f * 16 + l16;  // row within the column tile
+        st.q[f] = bload16(bf.q, kin ? (unsigned)row * (unsigned)a.K + (unsigned)kl : kOOB);
     }
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
-        const int64_t m = b * 16 + l16;
-        if (kin && m < a.M) {
-            const unsigned char *p = a.x + (m * a.K + kl) * 2;
-            st.x0[b] = load16(p);
-            st.x1[b] = load16(p + 16);
-        } else {
-            st.x0[b] = zero4();
-            st.x1[b] = zero4();
-        }
+        const unsigned off = kin ? ((unsigned)(b * 16 + l16) * (unsigned)a.K + (unsigned)kl) * 2u : kOOB;
+        st.x0[b] = bload16(bf.x, off);
+        st.x1[b] = bload16(bf.x, kin ? off + 16u : kOOB);
     }
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-        const int64_t rr = (int64_t)(wave + 4 * t) * 16 + l16;
-        if (kin && rr < a.r) {
-            const unsigned char *p = a.B + (rr * a.K + kl) * 2;
-            st.b0[t] = load16(p);
-            st.b1[t] = load16(p + 16);
-        } else {
-            st.b0[t] = zero4();
-            st.b1[t] = zero4();
-        }
+        const int rr = (wave + 4 * t) * 16 + l16;
+        const unsigned off = kin ? ((unsigned)rr * (unsigned)a.K + (unsigned)kl) * 2u : kOOB;
+        st.b0[t] = bload16(bf.b, off);
+        st.b1[t] = bload16(bf.b, kin ? off + 16u : kOOB);
     }
 }
 
@@ -111,9 +107,9 @@ __device__ __forceinline__ void compute_step(const Step<MB, RT> &st, f32x4 (&acc
 }
 
 template <bool OUT_F32>
-__device__ __forceinline__ void store_out(const SArgs &a, int64_t m, int64_t n, const float (&o)[4]) {
+__device__ __forceinline__ void store_out(const SArgs &a, int m, int n, const float (&o)[4]) {
     if (OUT_F32) {
-        float *dst = reinterpret_cast<float *>(a.y) + m * a.N + n;
+        float *dst = reinterpret_cast<float *>(a.y) + (int64_t)m * a.N + n;
         if (a.y_vec && n + 3 < a.N) {
             *reinterpret_cast<f32x4 *>(dst) = f32x4{o[0], o[1], o[2], o[3]};
         } else {
@@ -122,7 +118,7 @@ __device__ __forceinline__ void store_out(const SArgs &a, int64_t m, int64_t n, 
                 if (n + v < a.N) dst[v] = o[v];
         }
     } else {
-        unsigned short *dst = reinterpret_cast<unsigned short *>(a.y) + m * a.N + n;
+        unsigned short *dst = reinterpret_cast<unsigned short *>(a.y) + (int64_t)m * a.N + n;
         if (a.y_vec && n + 3 < a.N) {
             *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         } else {
@@ -135,15 +131,22 @@ __device__ __forceinline__ void store_out(const SArgs &a, int64_t m, int64_t n, 
 
 template <int MB, int RT, bool OUT_F32>
 __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
+    constexpr int DEPTH = RT <= 2 ? 3 : 2;  // K steps of loads in flight (register budget)
     constexpr int TS_LD = RT * 64 + 8;  // bf16 per LDS row of the T slice (16-byte multiple)
     __shared__ __attribute__((aligned(16))) unsigned short ts[MB * 16][TS_LD];
     __shared__ unsigned is_last;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
     const int tn = blockIdx.x, slice = blockIdx.y;
-    const int64_t nw = (int64_t)tn * SBN + wave * (WNF * 16);
-    const int64_t kb = (int64_t)slice * a.k_slice;
-    const int64_t ke = (kb + a.k_slice < a.K) ? kb + a.k_slice : a.K;
+    const int n_tile = tn * SBN, nw = n_tile + wave * (WNF * 16);
+    const int kb = slice * a.k_slice;
+    const int ke = (kb + a.k_slice < a.K) ? kb + a.k_slice : a.K;
+    const int rows_n = (a.N - n_tile) < SBN ? (a.N - n_tile) : SBN;
+
+    Bufs bf;
+    bf.q = make_rsrc(a.Q + (int64_t)n_tile * a.K, (int64_t)rows_n * a.K);
+    bf.x = make_rsrc(a.x, (int64_t)a.M * a.K * 2);
+    bf.b = make_rsrc(a.B, (int64_t)a.r * a.K * 2);
 
     f32x4 acc[WNF][MB], tacc[RT][MB];
 #pragma unroll
@@ -155,19 +158,23 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
 #pragma unroll
         for (int b = 0; b < MB; ++b) tacc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Reduction over this slice, loads for step k+64 in flight during step k.
-    Step<MB, RT> s0, s1;
-    if (kb < ke) load_step(s0, a, kb, ke, nw, wave, lane);
-    for (int64_t k = kb; k < ke; k += 128) {
-        if (k + 64 < ke) load_step(s1, a, k + 64, ke, nw, wave, lane);
-        compute_step(s0, acc, tacc);
-        if (k + 64 >= ke) break;
-        if (k + 128 < ke) load_step(s0, a, k + 128, ke, nw, wave, lane);
-        compute_step(s1, acc, tacc);
+    // Reduction over this slice with a ring of DEPTH register stages: the
+    // loads of step s + DEPTH - 1 are issued before step s is computed.
+    // Steps past the slice load zeros (out-of-range offsets) and add nothing.
+    const int nsteps = (ke - kb + 63) / 64;
+    Step<MB, RT> st[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d) load_step(st[d], bf, a, kb + 64 * d, ke, wave, lane);
+    for (int s0 = 0; s0 < nsteps; s0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            load_step(st[(d + DEPTH - 1) % DEPTH], bf, a, kb + 64 * (s0 + d + DEPTH - 1), ke, wave, lane);
+            compute_step(st[d], acc, tacc);
+        }
     }
 
     // T slice -> LDS as bf16: lane holds T[m = 16b + l16][16 rf + 4g + v].
-    const int rfr = (int)(a.r_pad / 16);
+    const int rfr = a.r_pad / 16;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
         const int rf = wave + 4 * t;
@@ -185,29 +192,18 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
 #pragma unroll
         for (int b = 0; b < MB; ++b) acc[f][b] *= a.scale;
 
-    // acc += T_slice A^T over the padded rank (A is read as zero past r).
-    for (int64_t k2 = 0; k2 < a.r_pad; k2 += 32) {
-        const int64_t ka = k2 + 8 * g;
+    // acc += T_slice A^T over the padded rank.  A rows are whole 16-byte
+    // chunks (lda % 8 == 0; zero padded past r), rows past N read as zero.
+    const rsrc_t ra = make_rsrc(a.A + (int64_t)n_tile * a.lda * 2, (int64_t)rows_n * a.lda * 2);
+    for (int k2 = 0; k2 < a.r_pad; k2 += 32) {
+        const int ka = k2 + 8 * g;
         u32x4 bt[MB];
 #pragma unroll
         for (int b = 0; b < MB; ++b) bt[b] = *reinterpret_cast<const u32x4 *>(&ts[b * 16 + l16][ka]);
 #pragma unroll
         for (int f = 0; f < WNF; ++f) {
-            const int64_t n = nw + f * 16 + l16;
-            u32x4 av = zero4();
-            if (n < a.N && ka < a.r) {
-                const unsigned char *p = a.A + (n * a.r + ka) * 2;
-                if (a.a_vec) {
-                    av = load16(p);
-                } else {
-                    unsigned short e[8];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t)
-                        e[t] = (ka + t < a.r) ? reinterpret_cast<const unsigned short *>(p)[t] : 0;
-                    av = u32x4{e[0] | (unsigned)e[1] << 16, e[2] | (unsigned)e[3] << 16,
-                               e[4] | (unsigned)e[5] << 16, e[6] | (unsigned)e[7] << 16};
-                }
-            }
+            const int row = wave * (WNF * 16) + f * 16 + l16;
+            const u32x4 av = bload16(ra, ka < a.lda ? ((unsigned)row * (unsigned)a.lda + (unsigned)ka) * 2u : kOOB);
 #pragma unroll
             for (int b = 0; b < MB; ++b) acc[f][b] = mfma16(av, bt[b], acc[f][b]);
         }
@@ -215,38 +211,32 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
 
     // Lane holds acc[f][b][v] = y[m = 16b + l16][n = nw + 16f + 4g + v] (minus bias).
     if (a.splits > 1) {
+        // Element-wise device-scope stores (relaxed atomics): visible to
+        // every XCD once they complete.
 #pragma unroll
         for (int f = 0; f < WNF; ++f) {
-            const int64_t n = nw + f * 16 + 4 * g;
+            const int n = nw + f * 16 + 4 * g;
 #pragma unroll
             for (int b = 0; b < MB; ++b) {
-                const int64_t m = b * 16 + l16;
+                const int m = b * 16 + l16;
                 if (m >= a.M) continue;
                 float *dst = a.partials + ((int64_t)slice * a.M + m) * a.N + n;
-                if (a.y_vec && n + 3 < a.N) {
-                    *reinterpret_cast<f32x4 *>(dst) = acc[f][b];
-                } else {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        if (n + v < a.N) dst[v] = acc[f][b][v];
-                }
+                for (int v = 0; v < 4; ++v)
+                    if (n + v < a.N) __hip_atomic_store(dst + v, acc[f][b][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        __threadfence();
+        // The barrier waits for this work-group's stores to complete; only
+        // then does the counter move.
         __syncthreads();
-        if (tid == 0) {
-            const unsigned prev = atomicAdd(&a.counters[tn], 1u);
-            __threadfence();
-            is_last = (prev == (unsigned)(a.splits - 1)) ? 1u : 0u;
-        }
+        if (tid == 0) is_last = bump_u32(&a.counters[tn]) == (unsigned)(a.splits - 1) ? 1u : 0u;
         __syncthreads();
         if (!is_last) return;
-        __threadfence();
     }
 
 #pragma unroll
     for (int f = 0; f < WNF; ++f) {
-        const int64_t n = nw + f * 16 + 4 * g;
+        const int n = nw + f * 16 + 4 * g;
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
         if (a.bias) {
 #pragma unroll
@@ -255,23 +245,15 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
         }
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
-            const int64_t m = b * 16 + l16;
+            const int m = b * 16 + l16;
             if (m >= a.M) continue;
             float s[4] = {0.f, 0.f, 0.f, 0.f};
             if (a.splits > 1) {
                 for (int sl = 0; sl < a.splits; ++sl) {
                     const float *src = a.partials + ((int64_t)sl * a.M + m) * a.N + n;
-                    if (a.y_vec && n + 3 < a.N) {
-                        const f32x4 p = *reinterpret_cast<const f32x4 *>(src);
-                        s[0] += p[0];
-                        s[1] += p[1];
-                        s[2] += p[2];
-                        s[3] += p[3];
-                    } else {
 #pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            if (n + v < a.N) s[v] += src[v];
-                    }
+                    for (int v = 0; v < 4; ++v)
+                        if (n + v < a.N) s[v] += __hip_atomic_load(src + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             } else {
 #pragma unroll
@@ -294,7 +276,7 @@ hipError_t launch_sk(const SArgs &a, int tiles_n, hipStream_t s) {
 // register budget allows RT <= 8 / MB (larger combinations would spill).
 template <bool OUT_F32>
 hipError_t launch_sk_m(const SArgs &a, int tiles_n, hipStream_t s) {
-    const int64_t rt = (a.r_pad + 63) / 64;
+    const int rt = (a.r_pad + 63) / 64;
     if (a.M <= 16) {
         if (rt <= 1) return launch_sk<1, 1, OUT_F32>(a, tiles_n, s);
         if (rt <= 2) return launch_sk<1, 2, OUT_F32>(a, tiles_n, s);
@@ -323,6 +305,13 @@ bool skinny_supports(int64_t M, int64_t r_pad) {
     return false;
 }
 
+bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t splits) {
+    // Every buffer descriptor must stay below 2^31 bytes.
+    const int64_t lim = (int64_t)1 << 31;
+    return (int64_t)SBN * K < lim && M * K * 2 < lim && r_pad * K * 2 < lim && (int64_t)SBN * r_pad * 2 < lim &&
+           splits * M * N * 4 < lim;
+}
+
 int choose_skinny_splits(int64_t M, int64_t K, int64_t N) {
     (void)M;
     const int64_t tiles_n = (N + SBN - 1) / SBN;
@@ -333,25 +322,25 @@ int choose_skinny_splits(int64_t M, int64_t K, int64_t N) {
     return (int)s;
 }
 
-hipError_t launch_skinny(const SkinnyProblem &p, hipStream_t s) {
+hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t s) {
     SArgs a{};
     a.x = (const unsigned char *)p.x;
     a.B = (const unsigned char *)p.B;
     a.Q = (const unsigned char *)p.Q;
-    a.A = (const unsigned char *)p.A;
+    a.A = (const unsigned char *)a_eff;
     a.bias = (const unsigned char *)p.bias;
     a.y = p.y;
     a.partials = p.partials;
     a.counters = p.counters;
     a.scale = p.scale;
-    a.M = p.M;
-    a.K = p.K;
-    a.N = p.N;
-    a.r = p.r;
-    a.r_pad = p.r_pad;
-    a.k_slice = p.k_slice;
+    a.M = (int)p.M;
+    a.K = (int)p.K;
+    a.N = (int)p.N;
+    a.r = (int)p.r;
+    a.r_pad = (int)p.r_pad;
+    a.lda = a_eff == p.A ? (int)p.r : (int)p.r_pad;
+    a.k_slice = (int)p.k_slice;
     a.splits = p.splits;
-    a.a_vec = (p.r % 8 == 0) && ((uintptr_t)p.A % 16 == 0);
     a.y_vec = (p.N % 4 == 0) && ((uintptr_t)p.y % 16 == 0) && ((uintptr_t)p.partials % 16 == 0);
     const int tiles_n = (int)((p.N + SBN - 1) / SBN);
     return p.out_f32 ? launch_sk_m<true>(a, tiles_n, s) : launch_sk_m<false>(a, tiles_n, s);
