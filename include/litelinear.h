@@ -52,8 +52,10 @@ typedef enum {
     /* Output type.  0 = bf16 y (default, rounded to nearest even);
      * 1 = float32 y [M, out] (no output rounding; y must hold 4*M*out bytes). */
     LITELINEAR_OPT_OUTPUT_F32 = 2,
-    /* Skinny path K-split count.  0 = choose automatically, else the number
-     * of slices of `in` (clamped to [1, in/64]). */
+    /* Skinny path K-split hint.  0 = choose automatically, else the wanted
+     * number of slices of `in`; each slice is 256, 512 or 1024 elements of
+     * `in`, the smallest of these that does not give more slices than the
+     * hint (or 1024). */
     LITELINEAR_OPT_SPLIT_K = 3,
     /* Per-kernel timing.  1 = record a HIP event pair around every kernel
      * the handle launches, on the caller's stream; read the totals with

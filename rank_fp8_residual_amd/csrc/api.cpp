@@ -276,12 +276,8 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
     }
 
     if (path == 1) {
-        const int64_t ksteps = cdiv(in, 64);
-        int64_t splits = h->opt_split > 0 ? h->opt_split : ll::choose_skinny_splits(M, in, out);
-        if (splits > ksteps) splits = ksteps;
-        if (splits < 1) splits = 1;
-        const int64_t k_slice = cdiv(ksteps, splits) * 64;
-        splits = cdiv(in, k_slice);
+        const int64_t k_slice = 64 * (int64_t)ll::skinny_slice_steps(in, out, h->opt_split);
+        const int64_t splits = cdiv(in, k_slice);
         if (!ll::skinny_shape_ok(M, in, out, r_pad, splits)) return LITELINEAR_ERR_UNSUPPORTED;
         const int64_t tiles_n = cdiv(out, ll::skinny_col_tile());
         ll::SkinnyProblem p{};

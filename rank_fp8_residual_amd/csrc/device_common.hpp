@@ -69,7 +69,9 @@ __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr unsigned kOOB = 0x80000000u;  // an offset past every descriptor built here
+// Added to an offset to push it past every descriptor built here (all are
+// below 2^31 bytes, so real offset + kOOB is still out of range).
+constexpr unsigned kOOB = 0x80000000u;
 
 // Raw buffer over [base, base + bytes); bytes must stay below 2^31.
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
@@ -97,6 +99,17 @@ constexpr int kDeviceCoherent = 16;
 template <int POLICY = kCached>
 __device__ __forceinline__ void bload16_lds(rsrc_t r, void *lds, unsigned off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, off, 0, 0, POLICY);
+}
+
+// 16-byte device-coherent load, returned as a whole float vector: callers
+// only combine it as a vector (see bload16 on element extraction).
+__device__ __forceinline__ f32x4 bload16f_dc(rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceCoherent));
+}
+
+template <int POLICY>
+__device__ __forceinline__ void bstore16(rsrc_t r, unsigned off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, POLICY);
 }
 
 template <int POLICY>

@@ -48,14 +48,16 @@ struct SkinnyProblem {
     float scale;
     int64_t M, K, N, r, r_pad;
     int splits;          // number of K slices
-    int64_t k_slice;     // elements of K per slice (multiple of 64)
+    int64_t k_slice;     // elements of K per slice: 64 * skinny_slice_steps()
     bool out_f32;
 };
 
 int skinny_col_tile();                        // columns per work-group
 bool skinny_supports(int64_t M, int64_t r_pad);  // shapes the skinny kernel takes
 bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t splits);
-int choose_skinny_splits(int64_t M, int64_t K, int64_t N);
+// Steps of 64 per K slice (4, 8 or 16; the kernel unrolls them), aiming at
+// about one work-group per CU, or at `splits_hint` slices when it is > 0.
+int skinny_slice_steps(int64_t K, int64_t N, int64_t splits_hint);
 // a_eff: A itself, or its zero-padded [N, r_pad] copy (see a_needs_padding).
 hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t s);
 

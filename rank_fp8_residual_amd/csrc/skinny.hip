@@ -41,7 +41,7 @@ struct SArgs {
     unsigned *counters;
     float scale;
     int M, K, N, r, r_pad, lda, k_slice, splits;
-    bool y_vec;
+    bool y_vec, out_f32;
 };
 
 // Operands of one 64-wide step of the reduction, as this lane holds them:
@@ -63,24 +63,28 @@ __device__ __forceinline__ void load_step(Step<MB, RT> &st, const Bufs &bf, cons
                                           int wave, int lane) {
     const int l16 = lane & 15;
     const int kl = k + 16 * (lane >> 4);
-    const bool kin = kl < ke;  // in % 16 == 0: a 16-element chunk is all in or all out
+    // in % 16 == 0: a 16-element chunk is all in or all out.  Out-of-range
+    // chunks get offset + kOOB (past every descriptor) rather than one shared
+    // constant, so that no two loads become identical and get merged behind a
+    // branch: every load stays an unconditional instruction.
+    const unsigned oob = kl < ke ? 0u : kOOB;
 #pragma unroll
     for (int f = 0; f < WNF; ++f) {
         const int row = wave * (WNF * 16) + f * 16 + l16;  // row within the column tile
-        st.q[f] = bload16(bf.q, kin ? (unsigned)row * (unsigned)a.K + (unsigned)kl : kOOB);
+        st.q[f] = bload16(bf.q, (unsigned)row * (unsigned)a.K + (unsigned)kl + oob);
     }
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
-        const unsigned off = kin ? ((unsigned)(b * 16 + l16) * (unsigned)a.K + (unsigned)kl) * 2u : kOOB;
+        const unsigned off = ((unsigned)(b * 16 + l16) * (unsigned)a.K + (unsigned)kl) * 2u + oob;
         st.x0[b] = bload16(bf.x, off);
-        st.x1[b] = bload16(bf.x, kin ? off + 16u : kOOB);
+        st.x1[b] = bload16(bf.x, off + 16u);
     }
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
         const int rr = (wave + 4 * t) * 16 + l16;
-        const unsigned off = kin ? ((unsigned)rr * (unsigned)a.K + (unsigned)kl) * 2u : kOOB;
+        const unsigned off = ((unsigned)rr * (unsigned)a.K + (unsigned)kl) * 2u + oob;
         st.b0[t] = bload16(bf.b, off);
-        st.b1[t] = bload16(bf.b, kin ? off + 16u : kOOB);
+        st.b1[t] = bload16(bf.b, off + 16u);
     }
 }
 
@@ -106,9 +110,8 @@ __device__ __forceinline__ void compute_step(const Step<MB, RT> &st, f32x4 (&acc
         }
 }
 
-template <bool OUT_F32>
 __device__ __forceinline__ void store_out(const SArgs &a, int m, int n, const float (&o)[4]) {
-    if (OUT_F32) {
+    if (a.out_f32) {
         float *dst = reinterpret_cast<float *>(a.y) + (int64_t)m * a.N + n;
         if (a.y_vec && n + 3 < a.N) {
             *reinterpret_cast<f32x4 *>(dst) = f32x4{o[0], o[1], o[2], o[3]};
@@ -129,10 +132,21 @@ __device__ __forceinline__ void store_out(const SArgs &a, int m, int n, const fl
     }
 }
 
-template <int MB, int RT, bool OUT_F32>
+// Register stages of K steps in flight, from the per-step register cost
+// (Q 16, x 8 per row block, B 8 per rank fragment): deep enough to keep
+// ~32 KB per wave in flight, shallow enough not to spill.
+template <int MB, int RT>
+constexpr int skinny_depth() {
+    constexpr int regs = 16 + 8 * MB + 8 * RT;
+    constexpr int d = 200 / regs;
+    return d > 6 ? 6 : (d < 2 ? 2 : d);
+}
+
+template <int MB, int RT, int NSTEPS>
 __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
-    constexpr int DEPTH = RT <= 2 ? 3 : 2;  // K steps of loads in flight (register budget)
+    constexpr int DEPTH = skinny_depth<MB, RT>() < NSTEPS ? skinny_depth<MB, RT>() : NSTEPS;
     constexpr int TS_LD = RT * 64 + 8;  // bf16 per LDS row of the T slice (16-byte multiple)
+    constexpr int KCH = RT * 2;         // 32-wide rank chunks of A per fragment
     __shared__ __attribute__((aligned(16))) unsigned short ts[MB * 16][TS_LD];
     __shared__ unsigned is_last;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -147,6 +161,28 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
     bf.q = make_rsrc(a.Q + (int64_t)n_tile * a.K, (int64_t)rows_n * a.K);
     bf.x = make_rsrc(a.x, (int64_t)a.M * a.K * 2);
     bf.b = make_rsrc(a.B, (int64_t)a.r * a.K * 2);
+    // Built here, in uniform control flow, so that it stays in scalar
+    // registers (inside divergent code every use would become a loop).
+    const rsrc_t rp = make_rsrc(a.partials, (int64_t)a.splits * a.M * a.N * 4);
+
+    // A fragments for the epilogue: for ranks up to 128 they are fetched now,
+    // so their latency hides under the reduction (larger ranks load them per
+    // chunk at the end).  Lane holds A[row][32 c + 8 g, +8) for chunk c.  A
+    // rows are whole 16-byte chunks (lda % 8 == 0, zero padded past r); rows
+    // past N read as zero.
+    constexpr bool PREFETCH_A = RT <= 2;
+    const rsrc_t ra = make_rsrc(a.A + (int64_t)n_tile * a.lda * 2, (int64_t)rows_n * a.lda * 2);
+    auto load_a = [&](int f, int c) {
+        const int row = wave * (WNF * 16) + f * 16 + l16, ka = 32 * c + 8 * g;
+        return bload16(ra, ((unsigned)row * (unsigned)a.lda + (unsigned)ka) * 2u + (ka < a.lda ? 0u : kOOB));
+    };
+    u32x4 afr[WNF][PREFETCH_A ? KCH : 1];
+    if constexpr (PREFETCH_A) {
+#pragma unroll
+        for (int f = 0; f < WNF; ++f)
+#pragma unroll
+            for (int c = 0; c < KCH; ++c) afr[f][c] = load_a(f, c);
+    }
 
     f32x4 acc[WNF][MB], tacc[RT][MB];
 #pragma unroll
@@ -158,19 +194,21 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
 #pragma unroll
         for (int b = 0; b < MB; ++b) tacc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Reduction over this slice with a ring of DEPTH register stages: the
-    // loads of step s + DEPTH - 1 are issued before step s is computed.
-    // Steps past the slice load zeros (out-of-range offsets) and add nothing.
-    const int nsteps = (ke - kb + 63) / 64;
+    // Reduction over this slice (NSTEPS steps of 64, fully unrolled) with a
+    // ring of DEPTH register stages: the loads of step s + DEPTH - 1 are
+    // issued before step s is computed, and scheduling barriers keep the
+    // compiler from sinking them next to their uses.  Steps past the end of
+    // `in` load zeros (out-of-range offsets) and add nothing.
     Step<MB, RT> st[DEPTH];
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d) load_step(st[d], bf, a, kb + 64 * d, ke, wave, lane);
-    for (int s0 = 0; s0 < nsteps; s0 += DEPTH) {
 #pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            load_step(st[(d + DEPTH - 1) % DEPTH], bf, a, kb + 64 * (s0 + d + DEPTH - 1), ke, wave, lane);
-            compute_step(st[d], acc, tacc);
-        }
+    for (int s0 = 0; s0 < NSTEPS; ++s0) {
+        if (s0 + DEPTH - 1 < NSTEPS)
+            load_step(st[(s0 + DEPTH - 1) % DEPTH], bf, a, kb + 64 * (s0 + DEPTH - 1), ke, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_step(st[s0 % DEPTH], acc, tacc);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // T slice -> LDS as bf16: lane holds T[m = 16b + l16][16 rf + 4g + v].
@@ -192,18 +230,17 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
 #pragma unroll
         for (int b = 0; b < MB; ++b) acc[f][b] *= a.scale;
 
-    // acc += T_slice A^T over the padded rank.  A rows are whole 16-byte
-    // chunks (lda % 8 == 0; zero padded past r), rows past N read as zero.
-    const rsrc_t ra = make_rsrc(a.A + (int64_t)n_tile * a.lda * 2, (int64_t)rows_n * a.lda * 2);
-    for (int k2 = 0; k2 < a.r_pad; k2 += 32) {
-        const int ka = k2 + 8 * g;
+    // acc += T_slice A^T over the padded rank (A columns past r are zero).
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+        const int ka = 32 * c + 8 * g;
+        if (32 * c >= a.r_pad) break;
         u32x4 bt[MB];
 #pragma unroll
         for (int b = 0; b < MB; ++b) bt[b] = *reinterpret_cast<const u32x4 *>(&ts[b * 16 + l16][ka]);
 #pragma unroll
         for (int f = 0; f < WNF; ++f) {
-            const int row = wave * (WNF * 16) + f * 16 + l16;
-            const u32x4 av = bload16(ra, ka < a.lda ? ((unsigned)row * (unsigned)a.lda + (unsigned)ka) * 2u : kOOB);
+            const u32x4 av = PREFETCH_A ? afr[f][PREFETCH_A ? c : 0] : load_a(f, c);
 #pragma unroll
             for (int b = 0; b < MB; ++b) acc[f][b] = mfma16(av, bt[b], acc[f][b]);
         }
@@ -211,23 +248,29 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
 
     // Lane holds acc[f][b][v] = y[m = 16b + l16][n = nw + 16f + 4g + v] (minus bias).
     if (a.splits > 1) {
-        // Element-wise device-scope stores (relaxed atomics): visible to
-        // every XCD once they complete.
+        // Device-scope stores: visible to every XCD once they complete.
 #pragma unroll
         for (int f = 0; f < WNF; ++f) {
             const int n = nw + f * 16 + 4 * g;
 #pragma unroll
             for (int b = 0; b < MB; ++b) {
                 const int m = b * 16 + l16;
-                if (m >= a.M) continue;
-                float *dst = a.partials + ((int64_t)slice * a.M + m) * a.N + n;
+                if (m >= a.M || n >= a.N) continue;
+                if (a.y_vec) {  // out % 4 == 0: whole 16-byte groups
+                    bstore16<kDeviceCoherent>(rp, (unsigned)(((int64_t)slice * a.M + m) * a.N + n) * 4u,
+                                              __builtin_bit_cast(u32x4, acc[f][b]));
+                } else {
+                    float *dst = a.partials + ((int64_t)slice * a.M + m) * a.N + n;
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (n + v < a.N) __hip_atomic_store(dst + v, acc[f][b][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int v = 0; v < 4; ++v)
+                        if (n + v < a.N)
+                            __hip_atomic_store(dst + v, acc[f][b][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
         }
-        // The barrier waits for this work-group's stores to complete; only
-        // then does the counter move.
+        // Every wave waits for its own stores to complete (device scope),
+        // then the barrier; only then does the counter move.
+        wait_vmcnt<0>();
         __syncthreads();
         if (tid == 0) is_last = bump_u32(&a.counters[tn]) == (unsigned)(a.splits - 1) ? 1u : 0u;
         __syncthreads();
@@ -249,46 +292,76 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
             if (m >= a.M) continue;
             float s[4] = {0.f, 0.f, 0.f, 0.f};
             if (a.splits > 1) {
-                for (int sl = 0; sl < a.splits; ++sl) {
-                    const float *src = a.partials + ((int64_t)sl * a.M + m) * a.N + n;
+                if (n >= a.N) continue;
+                if (a.y_vec) {
+                    // Slices in batches of 8 whose loads are all in flight at
+                    // once (slices past the last read as zero), then summed in
+                    // slice order.
+                    const unsigned stride = (unsigned)a.M * (unsigned)a.N * 4u;
+                    const unsigned base = (unsigned)(m * a.N + n) * 4u;
+                    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int s0 = 0; s0 < a.splits; s0 += 8) {
+                        f32x4 p[8];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        if (n + v < a.N) s[v] += __hip_atomic_load(src + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        for (int u = 0; u < 8; ++u)
+                            p[u] = bload16f_dc(rp, base + (unsigned)(s0 + u) * stride + (s0 + u < a.splits ? 0u : kOOB));
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) sum += p[u];
+                    }
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) s[v] = sum[v];
+                } else {
+                    for (int sl = 0; sl < a.splits; ++sl) {
+                        const float *src = a.partials + ((int64_t)sl * a.M + m) * a.N + n;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            if (n + v < a.N)
+                                s[v] += __hip_atomic_load(src + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
                 }
             } else {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) s[v] = acc[f][b][v];
             }
             const float o[4] = {s[0] + bv[0], s[1] + bv[1], s[2] + bv[2], s[3] + bv[3]};
-            store_out<OUT_F32>(a, m, n, o);
+            store_out(a, m, n, o);
         }
     }
-    if (a.splits > 1 && tid == 0) a.counters[tn] = 0u;
+    if (a.splits > 1 && tid == 0) __hip_atomic_store(&a.counters[tn], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MB, int RT, bool OUT_F32>
+template <int MB, int RT, int NSTEPS>
 hipError_t launch_sk(const SArgs &a, int tiles_n, hipStream_t s) {
-    hipLaunchKernelGGL((skinny_kernel<MB, RT, OUT_F32>), dim3(tiles_n, a.splits), dim3(SNT), 0, s, a);
+    hipLaunchKernelGGL((skinny_kernel<MB, RT, NSTEPS>), dim3(tiles_n, a.splits), dim3(SNT), 0, s, a);
     return hipGetLastError();
+}
+
+template <int MB, int RT>
+hipError_t launch_sk_steps(const SArgs &a, int tiles_n, hipStream_t s) {
+    switch (a.k_slice / 64) {
+        case 4: return launch_sk<MB, RT, 4>(a, tiles_n, s);
+        case 8: return launch_sk<MB, RT, 8>(a, tiles_n, s);
+        case 16: return launch_sk<MB, RT, 16>(a, tiles_n, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 // Row blocks (MB) x rank fragments per wave (RT) that are instantiated: the
 // register budget allows RT <= 8 / MB (larger combinations would spill).
-template <bool OUT_F32>
 hipError_t launch_sk_m(const SArgs &a, int tiles_n, hipStream_t s) {
     const int rt = (a.r_pad + 63) / 64;
     if (a.M <= 16) {
-        if (rt <= 1) return launch_sk<1, 1, OUT_F32>(a, tiles_n, s);
-        if (rt <= 2) return launch_sk<1, 2, OUT_F32>(a, tiles_n, s);
-        if (rt <= 4) return launch_sk<1, 4, OUT_F32>(a, tiles_n, s);
-        if (rt <= 8) return launch_sk<1, 8, OUT_F32>(a, tiles_n, s);
+        if (rt <= 1) return launch_sk_steps<1, 1>(a, tiles_n, s);
+        if (rt <= 2) return launch_sk_steps<1, 2>(a, tiles_n, s);
+        if (rt <= 4) return launch_sk_steps<1, 4>(a, tiles_n, s);
+        if (rt <= 8) return launch_sk_steps<1, 8>(a, tiles_n, s);
     } else if (a.M <= 32) {
-        if (rt <= 1) return launch_sk<2, 1, OUT_F32>(a, tiles_n, s);
-        if (rt <= 2) return launch_sk<2, 2, OUT_F32>(a, tiles_n, s);
-        if (rt <= 4) return launch_sk<2, 4, OUT_F32>(a, tiles_n, s);
+        if (rt <= 1) return launch_sk_steps<2, 1>(a, tiles_n, s);
+        if (rt <= 2) return launch_sk_steps<2, 2>(a, tiles_n, s);
+        if (rt <= 4) return launch_sk_steps<2, 4>(a, tiles_n, s);
     } else if (a.M <= SMAX_M) {
-        if (rt <= 1) return launch_sk<4, 1, OUT_F32>(a, tiles_n, s);
-        if (rt <= 2) return launch_sk<4, 2, OUT_F32>(a, tiles_n, s);
+        if (rt <= 1) return launch_sk_steps<4, 1>(a, tiles_n, s);
+        if (rt <= 2) return launch_sk_steps<4, 2>(a, tiles_n, s);
     }
     return hipErrorInvalidValue;
 }
@@ -312,14 +385,13 @@ bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t spl
            splits * M * N * 4 < lim;
 }
 
-int choose_skinny_splits(int64_t M, int64_t K, int64_t N) {
-    (void)M;
+int skinny_slice_steps(int64_t K, int64_t N, int64_t splits_hint) {
     const int64_t tiles_n = (N + SBN - 1) / SBN;
     const int64_t ksteps = (K + 63) / 64;
-    int64_t s = (256 + tiles_n - 1) / tiles_n;  // about one work-group per CU
-    if (s > ksteps / 4) s = ksteps / 4;         // keep >= 4 steps of 64 per slice
-    if (s < 1) s = 1;
-    return (int)s;
+    int64_t want = splits_hint > 0 ? splits_hint : (256 + tiles_n - 1) / tiles_n;  // ~one work-group per CU
+    if (want < 1) want = 1;
+    const int64_t per = (ksteps + want - 1) / want;
+    return per <= 4 ? 4 : (per <= 8 ? 8 : 16);
 }
 
 hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t s) {
@@ -342,8 +414,9 @@ hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t 
     a.k_slice = (int)p.k_slice;
     a.splits = p.splits;
     a.y_vec = (p.N % 4 == 0) && ((uintptr_t)p.y % 16 == 0) && ((uintptr_t)p.partials % 16 == 0);
+    a.out_f32 = p.out_f32;
     const int tiles_n = (int)((p.N + SBN - 1) / SBN);
-    return p.out_f32 ? launch_sk_m<true>(a, tiles_n, s) : launch_sk_m<false>(a, tiles_n, s);
+    return launch_sk_m(a, tiles_n, s);
 }
 
 }  // namespace ll
