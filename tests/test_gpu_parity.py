@@ -77,6 +77,22 @@ def test_decode_every_code_bit_exact(dev, path):
     assert np.array_equal(y, expect)  # -0 == +0: a sum cannot keep the sign of a zero
 
 
+# ------------------------------------------------------ hand example
+
+@pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
+def test_hand_example(dev, path):
+    """The forward worked by hand in tests/golden/hand_example.json: float32
+    output must equal it exactly, bf16 output must be its nearest-even bf16."""
+    from tests.test_oracle_pins import load_hand_example
+    d, y_hand, _ = load_hand_example()
+    g = to_dev(d, dev)
+    say("hand example", path.name)
+    y32 = parity.to_f64(run(make_handle(dev, path, out_f32=True), g))
+    assert np.array_equal(y32, y_hand), (y32, y_hand)
+    y16 = parity.to_f64(run(make_handle(dev, path), g))
+    assert np.array_equal(y16, parity.bf16_of(y_hand)), (y16, y_hand)
+
+
 # ------------------------------------------------------- exact arithmetic
 
 EXACT_SHAPES = [  # M, in, out, r

@@ -15,6 +15,7 @@ by the mathematics and by independent library routines, never against itself.
 """
 from __future__ import annotations
 
+import json
 import math
 import os
 import tempfile
@@ -195,8 +196,39 @@ def check_invariants(lib):
                           fwd(x1)[rows])
 
 
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_hand_example():
+    """The hand-worked forward in tests/golden/hand_example.json as tensors."""
+    with open(os.path.join(GOLDEN, "hand_example.json")) as f:
+        g = json.load(f)
+    codes = np.array([[int(c, 16) for c in row] for row in g["Q_codes_hex"]], dtype=np.uint8)
+    d = {
+        "x": torch.tensor(g["x"], dtype=torch.float32).to(torch.bfloat16),
+        "A": torch.tensor(g["A"], dtype=torch.float32).to(torch.bfloat16),
+        "B": torch.tensor(g["B"], dtype=torch.float32).to(torch.bfloat16),
+        "Q": torch.from_numpy(codes),
+        "scale": float(g["scale"]),
+        "bias": torch.tensor(g["bias"], dtype=torch.float32).to(torch.bfloat16),
+        "M": g["M"], "in": g["in"], "out": g["out"], "r": g["r"],
+    }
+    return d, np.array(g["y"], dtype=np.float64), g
+
+
+def check_hand_example(lib):
+    d, y_hand, g = load_hand_example()
+    # the inputs are exact in bf16, and the code table matches the fixture's values
+    assert np.array_equal(_f64(d["x"]), np.array(g["x"], np.float64))
+    for code, v in g["Q_values"].items():
+        assert lib.oracle_e4m3fn_to_f64(int(code, 16)) == v, code
+    y = oracle.forward(d["x"], d["A"], d["B"], d["Q"], d["scale"], d["bias"], lib=lib)
+    assert np.array_equal(y, y_hand), (y, y_hand)
+
+
 PINS = [check_decode_vs_torch, check_lowrank_only, check_residual_only, check_r0,
-        check_dense_equivalence, check_bruteforce_rational, check_exact_integer, check_invariants]
+        check_dense_equivalence, check_bruteforce_rational, check_exact_integer, check_invariants,
+        check_hand_example]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
