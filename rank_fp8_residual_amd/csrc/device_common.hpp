@@ -85,6 +85,14 @@ __device__ __forceinline__ u32x4 bload16(rsrc_t r, unsigned off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// One bf16 element of a row (element index n, row held by r with 2 bytes per
+// element) as a float; past the row's end, or with an empty descriptor, it
+// reads as zero.  There is no branch, so a run of these loads stays in
+// flight together and costs one memory round trip.
+__device__ __forceinline__ float bload_bf16(rsrc_t r, unsigned n) {
+    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, n * 2u, 0, 0));
+}
+
 // Cache policy of a load or store.  kDeviceCoherent (the sc1 bit) makes a
 // load read, and a store write, at device scope: it never returns a line
 // that another XCD's L2 has made stale, and a store is complete (vmcnt)

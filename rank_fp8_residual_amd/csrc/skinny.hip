@@ -277,53 +277,87 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
         if (!is_last) return;
     }
 
+    // Bias of this lane's columns, fetched before the partial sums so that
+    // its latency overlaps theirs.
+    const rsrc_t rb = make_rsrc(a.bias, a.bias ? (int64_t)a.N * 2 : 0);
+    float bv[WNF][4];
 #pragma unroll
     for (int f = 0; f < WNF; ++f) {
         const int n = nw + f * 16 + 4 * g;
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (a.bias) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                if (n + v < a.N) bv[v] = bf16_to_f32(reinterpret_cast<const unsigned short *>(a.bias)[n + v]);
-        }
+        for (int v = 0; v < 4; ++v) bv[f][v] = bload_bf16(rb, (unsigned)(n + v));
+    }
+
+    if (a.splits > 1 && a.y_vec) {
+        // Slices in batches of SB whose loads (every fragment of the lane)
+        // are all in flight at once: one memory round trip per batch.  Each
+        // element adds its slices in slice order, starting from zero, so the
+        // sum does not depend on which work-group got here.  Out-of-range
+        // slices, rows and columns read as zero.
+        constexpr int SB = (32 / (WNF * MB)) > 0 ? 32 / (WNF * MB) : 1;
+        const unsigned stride = (unsigned)a.M * (unsigned)a.N * 4u;
+        f32x4 sum[WNF][MB];
 #pragma unroll
-        for (int b = 0; b < MB; ++b) {
-            const int m = b * 16 + l16;
-            if (m >= a.M) continue;
-            float s[4] = {0.f, 0.f, 0.f, 0.f};
-            if (a.splits > 1) {
-                if (n >= a.N) continue;
-                if (a.y_vec) {
-                    // Slices in batches of 8 whose loads are all in flight at
-                    // once (slices past the last read as zero), then summed in
-                    // slice order.
-                    const unsigned stride = (unsigned)a.M * (unsigned)a.N * 4u;
-                    const unsigned base = (unsigned)(m * a.N + n) * 4u;
-                    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-                    for (int s0 = 0; s0 < a.splits; s0 += 8) {
-                        f32x4 p[8];
+        for (int f = 0; f < WNF; ++f)
 #pragma unroll
-                        for (int u = 0; u < 8; ++u)
-                            p[u] = bload16f_dc(rp, base + (unsigned)(s0 + u) * stride + (s0 + u < a.splits ? 0u : kOOB));
+            for (int b = 0; b < MB; ++b) sum[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < a.splits; s0 += SB) {
+            f32x4 p[SB][WNF][MB];
 #pragma unroll
-                        for (int u = 0; u < 8; ++u) sum += p[u];
+            for (int u = 0; u < SB; ++u)
+#pragma unroll
+                for (int f = 0; f < WNF; ++f)
+#pragma unroll
+                    for (int b = 0; b < MB; ++b) {
+                        const int n = nw + f * 16 + 4 * g, m = b * 16 + l16;
+                        const bool ok = s0 + u < a.splits && m < a.M && n < a.N;
+                        p[u][f][b] = bload16f_dc(rp, (unsigned)(s0 + u) * stride + (unsigned)(m * a.N + n) * 4u +
+                                                         (ok ? 0u : kOOB));
                     }
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) s[v] = sum[v];
-                } else {
+            for (int u = 0; u < SB; ++u)
+#pragma unroll
+                for (int f = 0; f < WNF; ++f)
+#pragma unroll
+                    for (int b = 0; b < MB; ++b) sum[f][b] += p[u][f][b];
+        }
+#pragma unroll
+        for (int f = 0; f < WNF; ++f)
+#pragma unroll
+            for (int b = 0; b < MB; ++b) acc[f][b] = sum[f][b];
+    } else if (a.splits > 1) {
+        // Columns not in whole 16-byte groups: element loads, slice order.
+#pragma unroll
+        for (int f = 0; f < WNF; ++f) {
+            const int n = nw + f * 16 + 4 * g;
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+                const int m = b * 16 + l16;
+                f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (m < a.M && n < a.N) {
                     for (int sl = 0; sl < a.splits; ++sl) {
                         const float *src = a.partials + ((int64_t)sl * a.M + m) * a.N + n;
 #pragma unroll
                         for (int v = 0; v < 4; ++v)
                             if (n + v < a.N)
-                                s[v] += __hip_atomic_load(src + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                t[v] += __hip_atomic_load(src + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
-            } else {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) s[v] = acc[f][b][v];
+                acc[f][b] = t;
             }
-            const float o[4] = {s[0] + bv[0], s[1] + bv[1], s[2] + bv[2], s[3] + bv[3]};
+        }
+    }
+
+#pragma unroll
+    for (int f = 0; f < WNF; ++f) {
+        const int n = nw + f * 16 + 4 * g;
+        if (n >= a.N) continue;
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+            const int m = b * 16 + l16;
+            if (m >= a.M) continue;
+            const float o[4] = {acc[f][b][0] + bv[f][0], acc[f][b][1] + bv[f][1], acc[f][b][2] + bv[f][2],
+                                acc[f][b][3] + bv[f][3]};
             store_out(a, m, n, o);
         }
     }
@@ -382,7 +416,7 @@ bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t spl
     // Every buffer descriptor must stay below 2^31 bytes.
     const int64_t lim = (int64_t)1 << 31;
     return (int64_t)SBN * K < lim && M * K * 2 < lim && r_pad * K * 2 < lim && (int64_t)SBN * r_pad * 2 < lim &&
-           splits * M * N * 4 < lim;
+           splits * M * N * 4 < lim && N * 2 < lim;
 }
 
 int skinny_slice_steps(int64_t K, int64_t N, int64_t splits_hint) {
