@@ -50,7 +50,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--path", default="auto", choices=["auto", "skinny", "tiled"])
-    p.add_argument("--split-k", type=int, default=0)
+    p.add_argument("--split-k", type=int, default=0, help="skinny path: K-slice hint (0: automatic)")
+    p.add_argument("--t-splits", type=int, default=0, help="tiled path: K slices per T block (0: automatic)")
     return p.parse_args()
 
 
@@ -105,6 +106,7 @@ def main():
     h = Handle(0)
     h.set_option(Option.PATH, {"auto": Path.AUTO, "skinny": Path.SKINNY, "tiled": Path.TILED}[args.path])
     h.set_option(Option.SPLIT_K, args.split_k)
+    h.set_option(Option.T_SPLITS, args.t_splits)
 
     def step(i):
         g = sets[i % copies]

@@ -60,7 +60,12 @@ typedef enum {
     /* Per-kernel timing.  1 = record a HIP event pair around every kernel
      * the handle launches, on the caller's stream; read the totals with
      * litelinear_kernel_time().  0 = off (default). */
-    LITELINEAR_OPT_PROFILE = 4
+    LITELINEAR_OPT_PROFILE = 4,
+    /* Tiled path: K slices per 64-column block of T = x B^T.  0 = choose
+     * automatically (default); n > 0 = n slices (at most the number of
+     * 64-element steps of `in`), computed by separate work-groups and summed
+     * in slice order. */
+    LITELINEAR_OPT_T_SPLITS = 5
 } litelinear_option_t;
 
 /* Kernels whose time litelinear_kernel_time() reports. */

@@ -56,15 +56,17 @@ struct litelinear_ctx {
     int device = 0;
     void *t_ws = nullptr;
     size_t t_ws_bytes = 0;
-    unsigned *tile_sync = nullptr;  // tiled path: per-row-tile counters (flags, done)
+    unsigned *tile_sync = nullptr;  // tiled path: counters (per row tile and per T block)
     size_t tile_sync_bytes = 0;
+    float *t_part = nullptr;        // tiled path: K-slice partial sums of T
+    size_t t_part_bytes = 0;
     void *a_pad = nullptr;          // tiled path: zero-padded copy of A
     size_t a_pad_bytes = 0;
     float *partials = nullptr;
     size_t partials_bytes = 0;
     unsigned *counters = nullptr;
     size_t n_counters = 0;
-    int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0;
+    int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0, opt_t_splits = 0;
     Prof prof[kNumKernels];
     std::vector<hipEvent_t> event_pool;
 };
@@ -84,7 +86,9 @@ litelinear_status_t grow(void **p, size_t *have, size_t need, bool zero) {
         (void)hipGetLastError();
         return LITELINEAR_ERR_OOM;
     }
-    if (zero && hipMemset(*p, 0, need) != hipSuccess) return LITELINEAR_ERR_HIP;
+    // Zeroed before any kernel of any stream can use it.
+    if (zero && (hipMemset(*p, 0, need) != hipSuccess || hipDeviceSynchronize() != hipSuccess))
+        return LITELINEAR_ERR_HIP;
     *have = need;
     return LITELINEAR_OK;
 }
@@ -186,6 +190,7 @@ litelinear_status_t litelinear_destroy(litelinear_handle_t h) {
         if (hipDeviceSynchronize() != hipSuccess) st = LITELINEAR_ERR_HIP;
         if (h->t_ws) (void)hipFree(h->t_ws);
         if (h->tile_sync) (void)hipFree(h->tile_sync);
+        if (h->t_part) (void)hipFree(h->t_part);
         if (h->a_pad) (void)hipFree(h->a_pad);
         if (h->partials) (void)hipFree(h->partials);
         if (h->counters) (void)hipFree(h->counters);
@@ -218,6 +223,10 @@ litelinear_status_t litelinear_set_option(litelinear_handle_t h, int key, int64_
         case LITELINEAR_OPT_PROFILE:
             if (value != 0 && value != 1) return LITELINEAR_ERR_INVALID_ARG;
             h->opt_profile = value;
+            return LITELINEAR_OK;
+        case LITELINEAR_OPT_T_SPLITS:
+            if (value < 0 || value > 64) return LITELINEAR_ERR_INVALID_ARG;
+            h->opt_t_splits = value;
             return LITELINEAR_OK;
     }
     return LITELINEAR_ERR_INVALID_ARG;
@@ -325,19 +334,22 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
     p.out_f32 = out_f32;
     const ll::TileCfg mc = ll::choose_main_tile(p);
     if (!ll::tiled_shape_ok(p, mc)) return LITELINEAR_ERR_UNSUPPORTED;
-    unsigned *flags = nullptr, *done = nullptr;
     if (r > 0) {
         st = grow(&h->t_ws, &h->t_ws_bytes, (size_t)M * r_pad * 2, false);
         if (st != LITELINEAR_OK) return st;
         p.t_ws = h->t_ws;
-        const size_t tiles = (size_t)ll::tiled_row_tiles(p, mc);
-        st = grow((void **)&h->tile_sync, &h->tile_sync_bytes, 2 * tiles * sizeof(unsigned), true);
+        p.t_splits = ll::tiled_t_splits(p, mc, h->opt_t_splits);
+        if (p.t_splits > 1) {
+            st = grow((void **)&h->t_part, &h->t_part_bytes, (size_t)p.t_splits * M * r_pad * sizeof(float), false);
+            if (st != LITELINEAR_OK) return st;
+            p.t_part = h->t_part;
+        }
+        st = grow((void **)&h->tile_sync, &h->tile_sync_bytes,
+                  (size_t)ll::tiled_sync_words(p, mc) * sizeof(unsigned), true);
         if (st != LITELINEAR_OK) return st;
-        flags = h->tile_sync;
-        done = h->tile_sync + tiles;
     }
     return timed_launch(h, LITELINEAR_KERNEL_MAIN, stream,
-                        [&] { return ll::launch_tiled(p, mc, a_eff, flags, done, stream); });
+                        [&] { return ll::launch_tiled(p, mc, a_eff, h->tile_sync, stream); });
 }
 
 }  // extern "C"

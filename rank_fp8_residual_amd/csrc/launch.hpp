@@ -13,8 +13,10 @@ struct TiledProblem {
     const void *x, *A, *B, *Q, *bias;
     void *y;
     void *t_ws;          // bf16 [M, r_pad]; unused when r == 0
+    float *t_part;       // float32 [t_splits, M, r_pad] partial sums of T (t_splits > 1)
     float scale;
     int64_t M, K, N, r, r_pad;
+    int t_splits;        // K slices per T block (tiled_t_splits())
     bool out_f32;
 };
 
@@ -33,10 +35,16 @@ bool a_needs_padding(int64_t r, const void *A);
 bool tiled_shape_ok(const TiledProblem &p, TileCfg c);
 int tiled_row_tiles(const TiledProblem &p, TileCfg c);
 hipError_t launch_pad_a(const void *A, void *a_pad, int64_t N, int64_t r, int64_t r_pad, hipStream_t s);
-// flags / done: two arrays of tiled_row_tiles() counters, zero before the
-// launch and left at zero by it.
-hipError_t launch_tiled(const TiledProblem &p, TileCfg c, const void *a_eff, unsigned *flags, unsigned *done,
-                        hipStream_t s);
+// K slices per 64-column block of T: T is computed by tiled_row_tiles() x
+// (r_pad / 64) x t_splits producer work-groups, enough of them to finish
+// early but few enough to leave most CUs to the output tiles.
+// hint > 0 asks for that many slices (capped at the number of K steps).
+int tiled_t_splits(const TiledProblem &p, TileCfg c, int64_t hint);
+// sync: tiled_sync_words() counters, zero before the launch and left at zero
+// by it (per row tile: T blocks done, consumers past their wait; per T block:
+// slices done).
+int64_t tiled_sync_words(const TiledProblem &p, TileCfg c);
+hipError_t launch_tiled(const TiledProblem &p, TileCfg c, const void *a_eff, unsigned *sync, hipStream_t s);
 
 // Skinny path: split-K over `in`; every work-group computes its own slice of
 // T, and the last work-group of each column tile sums the slices in order.

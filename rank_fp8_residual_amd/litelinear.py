@@ -35,6 +35,7 @@ class Option(enum.IntEnum):
     OUTPUT_F32 = 2
     SPLIT_K = 3
     PROFILE = 4
+    T_SPLITS = 5
 
 
 class Path(enum.IntEnum):
