@@ -53,9 +53,9 @@ typedef enum {
      * 1 = float32 y [M, out] (no output rounding; y must hold 4*M*out bytes). */
     LITELINEAR_OPT_OUTPUT_F32 = 2,
     /* Skinny path K-split hint.  0 = choose automatically, else the wanted
-     * number of slices of `in`; each slice is 256, 512 or 1024 elements of
-     * `in`, the smallest of these that does not give more slices than the
-     * hint (or 1024). */
+     * number of slices of `in`; each slice is a power of two from 512 to
+     * 4096 elements of `in` (at most 4096 / ceil(M / 16)), the smallest that
+     * does not give more slices than the hint. */
     LITELINEAR_OPT_SPLIT_K = 3,
     /* Per-kernel timing.  1 = record a HIP event pair around every kernel
      * the handle launches, on the caller's stream; read the totals with
@@ -70,10 +70,10 @@ typedef enum {
 
 /* Kernels whose time litelinear_kernel_time() reports. */
 typedef enum {
-    LITELINEAR_KERNEL_PAD_A = 0,  /* copy of A into a zero-padded [out, r_pad] buffer (tiled path,
+    LITELINEAR_KERNEL_PAD_A = 0,  /* copy of A into a zero-padded [out, r_pad] buffer (either path,
                                      only when r % 8 != 0 or A is not 16-byte aligned) */
     LITELINEAR_KERNEL_MAIN = 1,   /* tiled path: T = x B^T, residual, rank-r product and bias */
-    LITELINEAR_KERNEL_SKINNY = 2  /* the skinny split-K kernel */
+    LITELINEAR_KERNEL_SKINNY = 2  /* skinny path: the same in one launch of its own kernel */
 } litelinear_kernel_t;
 
 /*

@@ -58,8 +58,12 @@ struct litelinear_ctx {
     size_t t_ws_bytes = 0;
     unsigned *tile_sync = nullptr;  // tiled path: counters (per row tile and per T block)
     size_t tile_sync_bytes = 0;
-    float *t_part = nullptr;        // tiled path: K-slice partial sums of T
+    float *t_part = nullptr;        // K-slice partial sums of T (both paths)
     size_t t_part_bytes = 0;
+    // Launches since the counters of each path were zeroed (their T-ready
+    // counters only grow, by a fixed step per launch).
+    unsigned tiled_epoch = 0, skinny_epoch = 0;
+    uint64_t tiled_key = 0, skinny_key = 0;  // layout the counters were last used with
     void *a_pad = nullptr;          // tiled path: zero-padded copy of A
     size_t a_pad_bytes = 0;
     float *partials = nullptr;
@@ -269,8 +273,11 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
 
     const int64_t r_pad = r > 0 ? cdiv(r, 64) * 64 : 0;
     int64_t path = h->opt_path;
-    if (path == 0) path = (in > 0 && M <= kSkinnyAutoMaxM && ll::skinny_supports(M, r_pad)) ? 1 : 2;
-    if (path == 1 && (in == 0 || !ll::skinny_supports(M, r_pad))) return LITELINEAR_ERR_UNSUPPORTED;
+    ll::SkinnyPlan plan{};
+    const bool skinny_ok = in > 0 && ll::skinny_supports(M) &&
+                           ll::skinny_shape_ok(M, in, out, r_pad, plan = ll::skinny_plan(M, in, out, r_pad, h->opt_split));
+    if (path == 0) path = (M <= kSkinnyAutoMaxM && skinny_ok) ? 1 : 2;
+    if (path == 1 && !skinny_ok) return LITELINEAR_ERR_UNSUPPORTED;
 
     // A whose rows are not whole 16-byte chunks is first copied into a
     // zero-padded [out, r_pad] buffer (both paths read A in 16-byte chunks).
@@ -285,11 +292,8 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
     }
 
     if (path == 1) {
-        const int64_t k_slice = 64 * (int64_t)ll::skinny_slice_steps(in, out, h->opt_split);
-        const int64_t splits = cdiv(in, k_slice);
-        if (!ll::skinny_shape_ok(M, in, out, r_pad, splits)) return LITELINEAR_ERR_UNSUPPORTED;
-        const int64_t tiles_n = cdiv(out, ll::skinny_col_tile());
         ll::SkinnyProblem p{};
+        p.plan = plan;
         p.x = x;
         p.A = A;
         p.B = B;
@@ -302,20 +306,39 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
         p.N = out;
         p.r = r;
         p.r_pad = r_pad;
-        p.splits = (int)splits;
-        p.k_slice = k_slice;
         p.out_f32 = out_f32;
-        if (splits > 1) {
-            st = grow((void **)&h->partials, &h->partials_bytes, (size_t)splits * M * out * sizeof(float), false);
+        if (p.plan.splits > 1) {
+            st = grow((void **)&h->partials, &h->partials_bytes, (size_t)p.plan.splits * M * out * sizeof(float),
+                      false);
             if (st != LITELINEAR_OK) return st;
-            size_t cbytes = h->n_counters * sizeof(unsigned);
-            st = grow((void **)&h->counters, &cbytes, (size_t)tiles_n * sizeof(unsigned), true);
-            if (st != LITELINEAR_OK) return st;
-            h->n_counters = cbytes / sizeof(unsigned);
             p.partials = h->partials;
-            p.counters = h->counters;
         }
-        return timed_launch(h, LITELINEAR_KERNEL_SKINNY, stream, [&] { return ll::launch_skinny(p, a_eff, stream); });
+        if (r > 0) {
+            st = grow((void **)&h->t_part, &h->t_part_bytes, (size_t)p.plan.t_splits * M * r_pad * sizeof(float),
+                      false);
+            if (st != LITELINEAR_OK) return st;
+            p.t_part = h->t_part;
+        }
+        size_t cbytes = h->n_counters * sizeof(unsigned);
+        const size_t need = (size_t)ll::skinny_sync_words(p.plan) * sizeof(unsigned);
+        if (cbytes < need) h->skinny_epoch = 0;  // counters start again from zero
+        st = grow((void **)&h->counters, &cbytes, need, true);
+        if (st != LITELINEAR_OK) return st;
+        h->n_counters = cbytes / sizeof(unsigned);
+        p.sync = h->counters;
+        // The T flag sits after the column-tile counters: a new layout or
+        // step (with or without T) starts every counter again from zero, so
+        // no word ever holds another layout's flag.
+        const uint64_t key = ((uint64_t)p.plan.tiles_n << 32) | (uint64_t)(r > 0 ? p.plan.pps * p.plan.splits : 0);
+        if (key != h->skinny_key) {
+            if (hipMemsetAsync(h->counters, 0, cbytes, stream) != hipSuccess) return LITELINEAR_ERR_HIP;
+            h->skinny_key = key;
+            h->skinny_epoch = 0;
+        }
+        p.t_target = (h->skinny_epoch + 1u) * (unsigned)(p.plan.pps * p.plan.splits);
+        st = timed_launch(h, LITELINEAR_KERNEL_SKINNY, stream, [&] { return ll::launch_skinny(p, a_eff, stream); });
+        if (st == LITELINEAR_OK && r > 0) ++h->skinny_epoch;
+        return st;
     }
 
     ll::TiledProblem p{};
@@ -344,12 +367,25 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
             if (st != LITELINEAR_OK) return st;
             p.t_part = h->t_part;
         }
-        st = grow((void **)&h->tile_sync, &h->tile_sync_bytes,
-                  (size_t)ll::tiled_sync_words(p, mc) * sizeof(unsigned), true);
+        const size_t need = (size_t)ll::tiled_sync_words(p, mc) * sizeof(unsigned);
+        if (h->tile_sync_bytes < need) h->tiled_epoch = 0;  // counters start again from zero
+        st = grow((void **)&h->tile_sync, &h->tile_sync_bytes, need, true);
         if (st != LITELINEAR_OK) return st;
+        // The ready counters of every row tile must have grown by the same
+        // step in every launch so far; a different row-tile count or step
+        // starts them again from zero (ordered on the stream).
+        const uint64_t key = ((uint64_t)ll::tiled_row_tiles(p, mc) << 32) | ll::tiled_flag_step(p);
+        if (key != h->tiled_key) {
+            if (hipMemsetAsync(h->tile_sync, 0, h->tile_sync_bytes, stream) != hipSuccess) return LITELINEAR_ERR_HIP;
+            h->tiled_key = key;
+            h->tiled_epoch = 0;
+        }
+        p.t_target = (h->tiled_epoch + 1u) * ll::tiled_flag_step(p);
     }
-    return timed_launch(h, LITELINEAR_KERNEL_MAIN, stream,
-                        [&] { return ll::launch_tiled(p, mc, a_eff, h->tile_sync, stream); });
+    st = timed_launch(h, LITELINEAR_KERNEL_MAIN, stream,
+                      [&] { return ll::launch_tiled(p, mc, a_eff, h->tile_sync, stream); });
+    if (st == LITELINEAR_OK && r > 0) ++h->tiled_epoch;
+    return st;
 }
 
 }  // extern "C"

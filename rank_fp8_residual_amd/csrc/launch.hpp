@@ -17,6 +17,7 @@ struct TiledProblem {
     float scale;
     int64_t M, K, N, r, r_pad;
     int t_splits;        // K slices per T block (tiled_t_splits())
+    unsigned t_target;   // row-tile counter value that marks this launch's T done
     bool out_f32;
 };
 
@@ -40,32 +41,49 @@ hipError_t launch_pad_a(const void *A, void *a_pad, int64_t N, int64_t r, int64_
 // early but few enough to leave most CUs to the output tiles.
 // hint > 0 asks for that many slices (capped at the number of K steps).
 int tiled_t_splits(const TiledProblem &p, TileCfg c, int64_t hint);
-// sync: tiled_sync_words() counters, zero before the launch and left at zero
-// by it (per row tile: T blocks done, consumers past their wait; per T block:
-// slices done).
+// sync: tiled_sync_words() counters, zero when allocated.  Per row tile, the
+// number of finished T blocks over all launches: it grows by
+// tiled_flag_step() per launch, so launch number e (from 1, counted since the
+// counters were zeroed) sets t_target = e * tiled_flag_step() (mod 2^32).
+// Per T block, finished K slices (left at zero by every launch).
 int64_t tiled_sync_words(const TiledProblem &p, TileCfg c);
+unsigned tiled_flag_step(const TiledProblem &p);
 hipError_t launch_tiled(const TiledProblem &p, TileCfg c, const void *a_eff, unsigned *sync, hipStream_t s);
 
-// Skinny path: split-K over `in`; every work-group computes its own slice of
-// T, and the last work-group of each column tile sums the slices in order.
+// Skinny path (M <= 64): T producers plus output work-groups of 128
+// columns over K slices (see skinny.hip).
+struct SkinnyPlan {
+    int mb;          // row blocks of 16 (1, 2 or 4)
+    int k_slice;     // K elements per output work-group (512 .. 4096)
+    int splits;      // K slices
+    int tiles_n;     // column tiles
+    int groups;      // 16-rank fragments of T (r_pad / 16)
+    int t_kslice;    // K elements of a T piece
+    int t_splits;    // K ranges of T pieces (over all slices)
+    int pps;         // T pieces per K slice
+    int pwg;         // work-groups per slice that compute pieces
+    int producers;   // pwg * splits when r > 0: the pieces' work-groups
+};
+
 struct SkinnyProblem {
     const void *x, *A, *B, *Q, *bias;
     void *y;
-    float *partials;     // float32 [splits, M, N] (used when splits > 1)
-    unsigned *counters;  // one per column tile, zero between calls
+    float *partials;     // float32 [splits, M, N] (splits > 1)
+    unsigned *sync;      // skinny_sync_words() counters, zero when allocated
+    unsigned t_target;   // launch number e (from 1, since the counters were
+                         // zeroed) times plan.producers, mod 2^32
+    float *t_part;       // T pieces, float32 [t_splits, M, r_pad] (r > 0)
     float scale;
     int64_t M, K, N, r, r_pad;
-    int splits;          // number of K slices
-    int64_t k_slice;     // elements of K per slice: 64 * skinny_slice_steps()
     bool out_f32;
+    SkinnyPlan plan;
 };
 
-int skinny_col_tile();                        // columns per work-group
-bool skinny_supports(int64_t M, int64_t r_pad);  // shapes the skinny kernel takes
-bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t splits);
-// Steps of 64 per K slice (4, 8 or 16; the kernel unrolls them), aiming at
-// about one work-group per CU, or at `splits_hint` slices when it is > 0.
-int skinny_slice_steps(int64_t K, int64_t N, int64_t splits_hint);
+bool skinny_supports(int64_t M);  // row counts the skinny kernel takes
+// splits_hint > 0 asks for about that many K slices.
+SkinnyPlan skinny_plan(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t splits_hint);
+int64_t skinny_sync_words(const SkinnyPlan &pl);
+bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, const SkinnyPlan &pl);
 // a_eff: A itself, or its zero-padded [N, r_pad] copy (see a_needs_padding).
 hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t s);
 

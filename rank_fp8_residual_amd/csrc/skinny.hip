@@ -4,111 +4,61 @@
 // the introduction):  y = (x B^T) A^T + scale * (x dec(Q)^T) + bias.
 //
 // With few rows the time is the time to stream Q (out * in bytes) from HBM
-// once.  The reduction over `in` is split into slices so that enough
-// work-groups run to keep every CU loading; the grid is
-// (column tiles of 256 outputs) x (K slices).  A work-group:
-//   * streams its 256 x k_slice block of Q codes with 128-bit buffer loads
-//     straight into registers (16 codes per lane per fragment), D steps of 64
-//     ahead, converts them exactly to bf16 and feeds
-//     v_mfma_f32_16x16x32_bf16 against the x rows;
-//   * computes its slice's share of T = x B^T on the same x registers
-//     (T = sum over slices of T_slice, so (sum T_slice) A^T = sum T_slice A^T
-//     and no separate pass over x is needed);
-//   * forms scale * acc + T_slice A^T, with T_slice rounded once to bf16;
-//   * writes that partial sum as float32 with device-coherent stores; the
-//     last work-group of the column tile to finish (an atomic counter) reads
-//     the slices back with device-coherent loads, adds them in slice order,
-//     adds bias and stores y.  The result does not depend on which
-//     work-group finishes last, and the counter is left at zero.
-// With one slice the partial step is skipped and y is stored directly.
-// Every load is a buffer load: reads past a descriptor's end return zero,
-// so masking rows, columns and the K tail needs no branch.
+// once, so the launch is organised around that stream:
+//   * Work-groups own 128 output columns over one K slice.  Each copies its
+//     slice of x into LDS once (buffer loads straight to LDS), then its four
+//     waves stream their 32 columns of Q codes with 128-bit loads into
+//     registers, DEPTH steps of 64 ahead, convert them exactly to bf16 and
+//     feed v_mfma_f32_16x16x32_bf16 against the x rows read from LDS.
+//   * When r > 0 the lowest-id work-groups of each slice also compute pieces
+//     of T = x B^T (16 ranks over part of their slice, x from the same LDS)
+//     before their Q stream starts: float32, summed over the four waves in
+//     wave order, stored with device-coherent stores; each piece bumps a flag.
+//   * With several K slices each output work-group writes its partial sum
+//     (float32, device-coherent stores); the last one of a column tile to
+//     finish (an atomic counter) adds the slices in slice order, so the
+//     result does not depend on which one finishes last.
+//   * That last work-group then waits for T (long since done), adds the
+//     pieces of T in K order, rounds T once to bf16, forms
+//     scale * sum + T A^T + bias and stores y.  The slice counters are left
+//     at zero; the T flag only grows, by the producer count per launch, and
+//     each launch waits for its own target value.
+// Only final work-groups wait, and only for T pieces.  The piece work-groups
+// have the lowest ids (at most one per CU), so they are dispatched first and
+// compute their pieces before waiting for anything: the waits always end.
+// Every global load is a buffer load: reads past a descriptor's end return
+// zero, so masking rows, columns and the K tail needs no branch.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace ll {
 namespace {
 
-constexpr int SNT = 256;            // threads per work-group (4 waves)
-constexpr int WNF = 4;              // 16-column fragments per wave
-constexpr int SBN = 4 * WNF * 16;   // output columns per work-group
-constexpr int SMAX_M = 64;          // largest M (4 row blocks of 16)
+constexpr int SNT = 256;           // threads per work-group (4 waves)
+constexpr int WNF = 2;             // 16-column fragments per wave
+constexpr int SBN = 4 * WNF * 16;  // output columns per work-group
+constexpr int SMAX_M = 64;         // largest M (4 row blocks of 16)
+constexpr int DEPTH = 8;           // K steps of Q in flight per wave
+constexpr int TCH = 256;           // K elements per producer load round
+constexpr int XPAD = 8;            // bf16 of padding per LDS row of x
+constexpr int LDS_MAX = 160 * 1024;
 
 struct SArgs {
     const unsigned char *x, *B, *Q, *A, *bias;
     void *y;
-    float *partials;
-    unsigned *counters;
+    float *partials;     // [splits, M, N]
+    unsigned *cnt;       // [tiles_n] K slices done per column tile
+    unsigned *tflag;     // T pieces finished, counted over all launches
+    unsigned t_target;   // tflag value meaning "this launch's T is complete" (mod 2^32)
+    float *tpart;        // T pieces, float32 [t_splits, r_pad / 16, M, 16]
     float scale;
-    int M, K, N, r, r_pad, lda, k_slice, splits;
+    int M, K, N, r, r_pad, lda, splits, tiles_n, t_splits;
+    int pps;             // T pieces per K slice (16 ranks x a part of the slice each)
+    int pwg;             // work-groups of a slice that compute pieces (lowest ids)
     bool y_vec, out_f32;
 };
 
-// Operands of one 64-wide step of the reduction, as this lane holds them:
-// lane l covers reduction elements [k + 16*(l/16), +16) of row (l % 16) of
-// each 16-row fragment; both halves of 8 feed one matrix-core product each.
-template <int MB, int RT>
-struct Step {
-    u32x4 q[WNF];              // 16 e4m3fn codes per Q fragment
-    u32x4 x0[MB], x1[MB];      // 2 x 8 bf16 of x per row block
-    u32x4 b0[RT], b1[RT];      // 2 x 8 bf16 of B per rank fragment
-};
-
-struct Bufs {
-    rsrc_t q, x, b;
-};
-
-template <int MB, int RT>
-__device__ __forceinline__ void load_step(Step<MB, RT> &st, const Bufs &bf, const SArgs &a, int k, int ke,
-                                          int wave, int lane) {
-    const int l16 = lane & 15;
-    const int kl = k + 16 * (lane >> 4);
-    // in % 16 == 0: a 16-element chunk is all in or all out.  Out-of-range
-    // chunks get offset + kOOB (past every descriptor) rather than one shared
-    // constant, so that no two loads become identical and get merged behind a
-    // branch: every load stays an unconditional instruction.
-    const unsigned oob = kl < ke ? 0u : kOOB;
-#pragma unroll
-    for (int f = 0; f < WNF; ++f) {
-        const int row = wave * (WNF * 16) + f * 16 + l16;  // row within the column tile
-        st.q[f] = bload16(bf.q, (unsigned)row * (unsigned)a.K + (unsigned)kl + oob);
-    }
-#pragma unroll
-    for (int b = 0; b < MB; ++b) {
-        const unsigned off = ((unsigned)(b * 16 + l16) * (unsigned)a.K + (unsigned)kl) * 2u + oob;
-        st.x0[b] = bload16(bf.x, off);
-        st.x1[b] = bload16(bf.x, off + 16u);
-    }
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-        const int rr = (wave + 4 * t) * 16 + l16;
-        const unsigned off = ((unsigned)rr * (unsigned)a.K + (unsigned)kl) * 2u + oob;
-        st.b0[t] = bload16(bf.b, off);
-        st.b1[t] = bload16(bf.b, off + 16u);
-    }
-}
-
-template <int MB, int RT>
-__device__ __forceinline__ void compute_step(const Step<MB, RT> &st, f32x4 (&acc)[WNF][MB],
-                                             f32x4 (&tacc)[RT][MB]) {
-#pragma unroll
-    for (int f = 0; f < WNF; ++f) {
-        u32x4 h0, h1;
-        fp8x16_to_bf16x16(st.q[f], h0, h1);
-#pragma unroll
-        for (int b = 0; b < MB; ++b) {
-            acc[f][b] = mfma16(h0, st.x0[b], acc[f][b]);
-            acc[f][b] = mfma16(h1, st.x1[b], acc[f][b]);
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-        for (int b = 0; b < MB; ++b) {
-            tacc[t][b] = mfma16(st.b0[t], st.x0[b], tacc[t][b]);
-            tacc[t][b] = mfma16(st.b1[t], st.x1[b], tacc[t][b]);
-        }
-}
+// ------------------------------------------------------------ output tiles
 
 __device__ __forceinline__ void store_out(const SArgs &a, int m, int n, const float (&o)[4]) {
     if (a.out_f32) {
@@ -132,123 +82,197 @@ __device__ __forceinline__ void store_out(const SArgs &a, int m, int n, const fl
     }
 }
 
-// Register stages of K steps in flight, from the per-step register cost
-// (Q 16, x 8 per row block, B 8 per rank fragment): deep enough to keep
-// ~32 KB per wave in flight, shallow enough not to spill.
-template <int MB, int RT>
-constexpr int skinny_depth() {
-    constexpr int regs = 16 + 8 * MB + 8 * RT;
-    constexpr int d = 200 / regs;
-    return d > 6 ? 6 : (d < 2 ? 2 : d);
+template <int MB, int NSTEPS>
+constexpr int x_lds_bytes() {
+    return MB * 16 * (NSTEPS * 64 + XPAD) * 2;
 }
 
-template <int MB, int RT, int NSTEPS>
+// K elements of a T piece handled by one wave (a piece spans 4 of these).
+template <int NSTEPS>
+constexpr int t_kwave() {
+    return NSTEPS * 16 < 256 ? NSTEPS * 16 : 256;
+}
+
+template <int MB, int NSTEPS>
 __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
-    constexpr int DEPTH = skinny_depth<MB, RT>() < NSTEPS ? skinny_depth<MB, RT>() : NSTEPS;
-    constexpr int TS_LD = RT * 64 + 8;  // bf16 per LDS row of the T slice (16-byte multiple)
-    constexpr int KCH = RT * 2;         // 32-wide rank chunks of A per fragment
-    __shared__ __attribute__((aligned(16))) unsigned short ts[MB * 16][TS_LD];
-    __shared__ unsigned is_last;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, g = lane >> 4;
-    const int tn = blockIdx.x, slice = blockIdx.y;
-    const int n_tile = tn * SBN, nw = n_tile + wave * (WNF * 16);
-    const int kb = slice * a.k_slice;
-    const int ke = (kb + a.k_slice < a.K) ? kb + a.k_slice : a.K;
-    const int rows_n = (a.N - n_tile) < SBN ? (a.N - n_tile) : SBN;
+    constexpr int KS = NSTEPS * 64;            // K elements per slice
+    constexpr int XS = (KS + XPAD) * 2;        // LDS bytes per row of x
+    constexpr int D = DEPTH < NSTEPS ? DEPTH : NSTEPS;
+    constexpr int KW = t_kwave<NSTEPS>();      // K of a T piece per wave
+    constexpr int KP = 4 * KW;                 // K of a T piece
+    __shared__ __attribute__((aligned(16))) unsigned char xs[x_lds_bytes<MB, NSTEPS>()];
+    __shared__ f32x4 red[4 * MB * 64];
+    __shared__ unsigned is_last, tflag_sh;
 
-    Bufs bf;
-    bf.q = make_rsrc(a.Q + (int64_t)n_tile * a.K, (int64_t)rows_n * a.K);
-    bf.x = make_rsrc(a.x, (int64_t)a.M * a.K * 2);
-    bf.b = make_rsrc(a.B, (int64_t)a.r * a.K * 2);
-    // Built here, in uniform control flow, so that it stays in scalar
-    // registers (inside divergent code every use would become a loop).
-    const rsrc_t rp = make_rsrc(a.partials, (int64_t)a.splits * a.M * a.N * 4);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
+    // Work-group id -> (slice, column tile): the pwg piece work-groups of
+    // every slice come first.
+    const int c = (int)blockIdx.x;
+    int slice, tn;
+    const bool piece_wg = c < a.pwg * a.splits;
+    if (piece_wg) {
+        slice = c / a.pwg;
+        tn = c - slice * a.pwg;
+    } else {
+        const int c2 = c - a.pwg * a.splits, rest = a.tiles_n - a.pwg;
+        slice = c2 / rest;
+        tn = a.pwg + (c2 - slice * rest);
+    }
+    const int n0 = tn * SBN, nw = n0 + wave * (WNF * 16);
+    const int kb = slice * KS;
+    const int rows_n = (a.N - n0) < SBN ? (a.N - n0) : SBN;
 
-    // A fragments for the epilogue: for ranks up to 128 they are fetched now,
-    // so their latency hides under the reduction (larger ranks load them per
-    // chunk at the end).  Lane holds A[row][32 c + 8 g, +8) for chunk c.  A
-    // rows are whole 16-byte chunks (lda % 8 == 0, zero padded past r); rows
-    // past N read as zero.
-    constexpr bool PREFETCH_A = RT <= 2;
-    const rsrc_t ra = make_rsrc(a.A + (int64_t)n_tile * a.lda * 2, (int64_t)rows_n * a.lda * 2);
-    auto load_a = [&](int f, int c) {
-        const int row = wave * (WNF * 16) + f * 16 + l16, ka = 32 * c + 8 * g;
-        return bload16(ra, ((unsigned)row * (unsigned)a.lda + (unsigned)ka) * 2u + (ka < a.lda ? 0u : kOOB));
+    // Uniform descriptors (built here so they stay in scalar registers).
+    const rsrc_t rq = make_rsrc(a.Q + (int64_t)n0 * a.K, (int64_t)rows_n * a.K);
+    const rsrc_t rx = make_rsrc(a.x, (int64_t)a.M * a.K * 2);
+    const rsrc_t rp = make_rsrc(a.partials, a.splits > 1 ? (int64_t)a.splits * a.M * a.N * 4 : 0);
+    const rsrc_t rb = make_rsrc(a.bias, a.bias ? (int64_t)a.N * 2 : 0);
+
+    // Bias of this lane's columns, requested first (past N and a missing
+    // bias read as zero).
+    float bv[WNF][4];
+#pragma unroll
+    for (int f = 0; f < WNF; ++f)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) bv[f][v] = bload_bf16(rb, (unsigned)(nw + 16 * f + 4 * g + v));
+
+    // x[:, kb : kb + KS] -> LDS, rows of XS bytes (the padding puts the 16
+    // rows a fragment read touches on distinct banks).  One instruction
+    // moves 1 KB (512 elements) of one row; instruction i goes to wave i % 4.
+    {
+        constexpr int PER_ROW = KS / 512;
+        const int total = a.M * PER_ROW;
+        for (int i = wave; i < total; i += 4) {
+            const int row = i / PER_ROW, j = i - row * PER_ROW;
+            const int k = kb + 512 * j + 8 * lane;
+            const unsigned off = ((unsigned)row * (unsigned)a.K + (unsigned)k) * 2u + (k < a.K ? 0u : kOOB);
+            bload16_lds(rx, xs + row * XS + 1024 * j, off);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // T pieces: piece p of this slice is 16 ranks (fragment p % nfrag) over
+    // elements [KP (p / nfrag), +KP) of the slice; wave w takes quarter w.
+    // Lane holds B[16 f + l16][k + 8 g, +8) for its k steps of 32.
+    const int nfrag = a.r_pad / 16;
+    const rsrc_t rbm = make_rsrc(a.B, (int64_t)a.r * a.K * 2);
+    auto load_b = [&](u32x4 (&bb)[KW / 32], int p) {
+        const int f = p % nfrag, q = p / nfrag;
+#pragma unroll
+        for (int s2 = 0; s2 < KW / 32; ++s2) {
+            const int k = kb + q * KP + wave * KW + 32 * s2 + 8 * g;
+            bb[s2] = bload16(rbm, ((unsigned)(16 * f + l16) * (unsigned)a.K + (unsigned)k) * 2u + (k < a.K ? 0u : kOOB));
+        }
     };
-    u32x4 afr[WNF][PREFETCH_A ? KCH : 1];
-    if constexpr (PREFETCH_A) {
+    u32x4 bfirst[KW / 32];
+    const bool has_piece = piece_wg && a.r > 0;
+    if (has_piece) load_b(bfirst, tn);
+
+    // Q: lane holds codes [k + 16 g, +16) of row nw + 16 f + l16.
+    auto load_q = [&](u32x4 (&q)[WNF], int s) {
+        const int k = kb + 64 * s + 16 * g;
+        const unsigned oob = k < a.K ? 0u : kOOB;
 #pragma unroll
         for (int f = 0; f < WNF; ++f)
+            q[f] = bload16(rq, (unsigned)(wave * (WNF * 16) + 16 * f + l16) * (unsigned)a.K + (unsigned)k + oob);
+    };
+    u32x4 qr[D][WNF];
 #pragma unroll
-            for (int c = 0; c < KCH; ++c) afr[f][c] = load_a(f, c);
+    for (int s = 0; s < D - 1; ++s) load_q(qr[s], s);
+    // This wave's x copies (and B loads) are older than the D - 1 steps of
+    // Q loads just issued: once at most that many are in flight they have
+    // landed; the barrier then covers every wave's.
+    wait_vmcnt<(D - 1) * WNF>();
+    __syncthreads();
+
+    // This work-group's T pieces: 16 ranks x KW per wave from LDS x, the
+    // four quarters added in wave order through LDS by wave 0, stored
+    // device-coherent as float32 piece [slice (KS / KP) + p / nfrag][f][m][16].
+    if (has_piece) {
+        const rsrc_t rtp = make_rsrc(a.tpart, (int64_t)a.t_splits * nfrag * a.M * 16 * 4);
+        for (int p = tn; p < a.pps; p += a.pwg) {
+            u32x4 bb[KW / 32];
+            if (p == tn) {
+#pragma unroll
+                for (int s2 = 0; s2 < KW / 32; ++s2) bb[s2] = bfirst[s2];
+            } else {
+                load_b(bb, p);
+            }
+            const int f = p % nfrag, q = p / nfrag;
+            f32x4 tacc[MB];
+#pragma unroll
+            for (int b = 0; b < MB; ++b) tacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < KW / 32; ++s2) {
+                const int kk = q * KP + wave * KW + 32 * s2 + 8 * g;  // within the slice
+#pragma unroll
+                for (int b = 0; b < MB; ++b) {
+                    const u32x4 xv = *reinterpret_cast<const u32x4 *>(xs + (16 * b + l16) * XS + kk * 2);
+                    tacc[b] = mfma16(bb[s2], xv, tacc[b]);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < MB; ++b) red[(wave * MB + b) * 64 + lane] = tacc[b];
+            __syncthreads();
+            if (wave == 0) {
+                const int j = slice * (KS / KP) + q;
+#pragma unroll
+                for (int b = 0; b < MB; ++b) {
+                    f32x4 t = red[b * 64 + lane];
+#pragma unroll
+                    for (int w = 1; w < 4; ++w) t += red[(w * MB + b) * 64 + lane];
+                    const int m = 16 * b + l16;
+                    bstore16<kDeviceCoherent>(rtp, (unsigned)((((j * nfrag + f) * a.M + m) * 16 + 4 * g) * 4) +
+                                                       (m < a.M ? 0u : kOOB),
+                                              __builtin_bit_cast(u32x4, t));
+                }
+            }
+            __syncthreads();
+        }
     }
 
-    f32x4 acc[WNF][MB], tacc[RT][MB];
+    f32x4 acc[WNF][MB];
 #pragma unroll
     for (int f = 0; f < WNF; ++f)
 #pragma unroll
         for (int b = 0; b < MB; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-        for (int b = 0; b < MB; ++b) tacc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Reduction over this slice (NSTEPS steps of 64, fully unrolled) with a
-    // ring of DEPTH register stages: the loads of step s + DEPTH - 1 are
-    // issued before step s is computed, and scheduling barriers keep the
-    // compiler from sinking them next to their uses.  Steps past the end of
-    // `in` load zeros (out-of-range offsets) and add nothing.
-    Step<MB, RT> st[DEPTH];
+    // K loop, fully unrolled: the loads of step s + D - 1 are issued before
+    // step s is computed; scheduling barriers keep the compiler from sinking
+    // them next to their uses.  Steps past `in` load zeros and add nothing.
 #pragma unroll
-    for (int d = 0; d < DEPTH - 1; ++d) load_step(st[d], bf, a, kb + 64 * d, ke, wave, lane);
-#pragma unroll
-    for (int s0 = 0; s0 < NSTEPS; ++s0) {
-        if (s0 + DEPTH - 1 < NSTEPS)
-            load_step(st[(s0 + DEPTH - 1) % DEPTH], bf, a, kb + 64 * (s0 + DEPTH - 1), ke, wave, lane);
+    for (int s = 0; s < NSTEPS; ++s) {
+        if (s + D - 1 < NSTEPS) load_q(qr[(s + D - 1) % D], s + D - 1);
         __builtin_amdgcn_sched_barrier(0);
-        compute_step(st[s0 % DEPTH], acc, tacc);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // T slice -> LDS as bf16: lane holds T[m = 16b + l16][16 rf + 4g + v].
-    const int rfr = a.r_pad / 16;
+        u32x4 x0[MB], x1[MB];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-        const int rf = wave + 4 * t;
-        if (rf < rfr) {
-#pragma unroll
-            for (int b = 0; b < MB; ++b)
-                *reinterpret_cast<u32x2 *>(&ts[b * 16 + l16][rf * 16 + 4 * g]) =
-                    u32x2{pack_bf16x2(tacc[t][b][0], tacc[t][b][1]), pack_bf16x2(tacc[t][b][2], tacc[t][b][3])};
+        for (int b = 0; b < MB; ++b) {
+            const unsigned char *p = xs + (16 * b + l16) * XS + (64 * s + 16 * g) * 2;
+            x0[b] = *reinterpret_cast<const u32x4 *>(p);
+            x1[b] = *reinterpret_cast<const u32x4 *>(p + 16);
         }
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int f = 0; f < WNF; ++f)
-#pragma unroll
-        for (int b = 0; b < MB; ++b) acc[f][b] *= a.scale;
-
-    // acc += T_slice A^T over the padded rank (A columns past r are zero).
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-        const int ka = 32 * c + 8 * g;
-        if (32 * c >= a.r_pad) break;
-        u32x4 bt[MB];
-#pragma unroll
-        for (int b = 0; b < MB; ++b) bt[b] = *reinterpret_cast<const u32x4 *>(&ts[b * 16 + l16][ka]);
 #pragma unroll
         for (int f = 0; f < WNF; ++f) {
-            const u32x4 av = PREFETCH_A ? afr[f][PREFETCH_A ? c : 0] : load_a(f, c);
+            u32x4 h0, h1;
+            fp8x16_to_bf16x16(qr[s % D][f], h0, h1);
 #pragma unroll
-            for (int b = 0; b < MB; ++b) acc[f][b] = mfma16(av, bt[b], acc[f][b]);
+            for (int b = 0; b < MB; ++b) {
+                acc[f][b] = mfma16(h0, x0[b], acc[f][b]);
+                acc[f][b] = mfma16(h1, x1[b], acc[f][b]);
+            }
         }
+        // Wave 0's piece stores were issued before the loads of step D - 1,
+        // which this step has waited for: the stores are complete (device
+        // scope) and the pieces can be announced.
+        if (s == D - 1 && has_piece && wave == 0 && lane == 0) {
+            for (int p = tn; p < a.pps; p += a.pwg) bump_u32(a.tflag);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Lane holds acc[f][b][v] = y[m = 16b + l16][n = nw + 16f + 4g + v] (minus bias).
+    // Lane holds acc[f][b][v] = (x dec(Q)^T)[m = 16 b + l16][n = nw + 16 f + 4 g + v]
+    // summed over this slice.
     if (a.splits > 1) {
-        // Device-scope stores: visible to every XCD once they complete.
 #pragma unroll
         for (int f = 0; f < WNF; ++f) {
             const int n = nw + f * 16 + 4 * g;
@@ -268,58 +292,106 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
                 }
             }
         }
-        // Every wave waits for its own stores to complete (device scope),
-        // then the barrier; only then does the counter move.
+        // Every wave waits for its own stores (device scope), then the
+        // barrier; only then does the counter move.
         wait_vmcnt<0>();
         __syncthreads();
-        if (tid == 0) is_last = bump_u32(&a.counters[tn]) == (unsigned)(a.splits - 1) ? 1u : 0u;
+        if (tid == 0) {
+            // The first look at the T flag rides along with the counter.
+            const unsigned last = bump_u32(&a.cnt[tn]) == (unsigned)(a.splits - 1) ? 1u : 0u;
+            tflag_sh = a.r > 0 ? poll_u32(a.tflag) : 0u;
+            is_last = last;
+        }
         __syncthreads();
         if (!is_last) return;
     }
 
-    // Bias of this lane's columns, fetched before the partial sums so that
-    // its latency overlaps theirs.
-    const rsrc_t rb = make_rsrc(a.bias, a.bias ? (int64_t)a.N * 2 : 0);
-    float bv[WNF][4];
+    // Final work-group of the column tile.  Everything it reads goes out in
+    // one round: the partial sums of the slices, the A rows and, if the T
+    // flag already showed this launch's pieces complete, the T pieces.
+    const unsigned tflag0 =
+        a.splits > 1 ? tflag_sh : (a.r > 0 ? __builtin_amdgcn_readfirstlane(poll_u32(a.tflag)) : 0u);
+    bool t_ready = a.r <= 0 || (int)(tflag0 - a.t_target) >= 0;
+
+    constexpr int SB = (32 / (WNF * MB)) > 0 ? 32 / (WNF * MB) : 1;  // slices per batch of loads
+    const unsigned pstride = (unsigned)a.M * (unsigned)a.N * 4u;
+    auto load_batch = [&](f32x4 (&p)[SB][WNF][MB], int s0) {
 #pragma unroll
-    for (int f = 0; f < WNF; ++f) {
-        const int n = nw + f * 16 + 4 * g;
+        for (int u = 0; u < SB; ++u)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) bv[f][v] = bload_bf16(rb, (unsigned)(n + v));
+            for (int f = 0; f < WNF; ++f)
+#pragma unroll
+                for (int b = 0; b < MB; ++b) {
+                    const int n = nw + f * 16 + 4 * g, m = b * 16 + l16;
+                    const bool ok = s0 + u < a.splits && m < a.M && n < a.N;
+                    p[u][f][b] = bload16f_dc(rp, (unsigned)(s0 + u) * pstride + (unsigned)(m * a.N + n) * 4u +
+                                                     (ok ? 0u : kOOB));
+                }
+    };
+    f32x4 pb[SB][WNF][MB];
+    const bool vec_sum = a.splits > 1 && a.y_vec;
+    if (vec_sum) load_batch(pb, 0);
+
+    // T A^T runs over the padded rank 64 at a time (two 32-rank chunks c).
+    // Lane holds A[n][64 h + 32 c + 8 g, +8) and, for T, the float32 pieces
+    // of ranks 8 (g % 2) .. +8 of fragment 4 h + 2 c + g / 2 of row
+    // m = 16 b + l16, JB K ranges per batch (ranges past the last read zero).
+    constexpr int JB = 8 / MB;
+    const rsrc_t ra = make_rsrc(a.A + (int64_t)n0 * a.lda * 2, (int64_t)rows_n * a.lda * 2);
+    const rsrc_t rtp = make_rsrc(a.tpart, (int64_t)a.t_splits * nfrag * a.M * 16 * 4);
+    auto load_a = [&](u32x4 (&af)[2][WNF], int h) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int f = 0; f < WNF; ++f) {
+                const int ka = 64 * h + 32 * c + 8 * g;
+                af[c][f] = bload16(ra, ((unsigned)(wave * (WNF * 16) + 16 * f + l16) * (unsigned)a.lda + (unsigned)ka) *
+                                               2u +
+                                           (ka < a.lda ? 0u : kOOB));
+            }
+    };
+    auto load_t = [&](f32x4 (&tl)[2][MB][JB][2], int h, int j0) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int frag = 4 * h + 2 * c + (g >> 1);
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+                const int m = 16 * b + l16;
+#pragma unroll
+                for (int u = 0; u < JB; ++u) {
+                    const int j = j0 + u;
+                    const unsigned off = (unsigned)((((j * nfrag + frag) * a.M + m) * 16 + 8 * (g & 1)) * 4) +
+                                         (m < a.M && j < a.t_splits ? 0u : kOOB);
+                    tl[c][b][u][0] = bload16f_dc(rtp, off);
+                    tl[c][b][u][1] = bload16f_dc(rtp, off + 16u);
+                }
+            }
+        }
+    };
+    u32x4 af0[2][WNF];
+    f32x4 tl0[2][MB][JB][2];
+    if (a.r > 0) {
+        load_a(af0, 0);
+        if (t_ready) load_t(tl0, 0, 0);
     }
 
-    if (a.splits > 1 && a.y_vec) {
-        // Slices in batches of SB whose loads (every fragment of the lane)
-        // are all in flight at once: one memory round trip per batch.  Each
-        // element adds its slices in slice order, starting from zero, so the
-        // sum does not depend on which work-group got here.  Out-of-range
-        // slices, rows and columns read as zero.
-        constexpr int SB = (32 / (WNF * MB)) > 0 ? 32 / (WNF * MB) : 1;
-        const unsigned stride = (unsigned)a.M * (unsigned)a.N * 4u;
+    // Sum of the slices, each element in slice order from zero.
+    if (vec_sum) {
         f32x4 sum[WNF][MB];
 #pragma unroll
         for (int f = 0; f < WNF; ++f)
 #pragma unroll
             for (int b = 0; b < MB; ++b) sum[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < a.splits; s0 += SB) {
-            f32x4 p[SB][WNF][MB];
+        for (int s0 = 0;;) {
 #pragma unroll
             for (int u = 0; u < SB; ++u)
 #pragma unroll
                 for (int f = 0; f < WNF; ++f)
 #pragma unroll
-                    for (int b = 0; b < MB; ++b) {
-                        const int n = nw + f * 16 + 4 * g, m = b * 16 + l16;
-                        const bool ok = s0 + u < a.splits && m < a.M && n < a.N;
-                        p[u][f][b] = bload16f_dc(rp, (unsigned)(s0 + u) * stride + (unsigned)(m * a.N + n) * 4u +
-                                                         (ok ? 0u : kOOB));
-                    }
-#pragma unroll
-            for (int u = 0; u < SB; ++u)
-#pragma unroll
-                for (int f = 0; f < WNF; ++f)
-#pragma unroll
-                    for (int b = 0; b < MB; ++b) sum[f][b] += p[u][f][b];
+                    for (int b = 0; b < MB; ++b) sum[f][b] += pb[u][f][b];
+            s0 += SB;
+            if (s0 >= a.splits) break;
+            load_batch(pb, s0);
         }
 #pragma unroll
         for (int f = 0; f < WNF; ++f)
@@ -349,6 +421,74 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
     }
 
 #pragma unroll
+    for (int f = 0; f < WNF; ++f)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[f][b] *= a.scale;
+
+    if (a.r > 0) {
+        if (!t_ready) {
+            // The piece work-groups have the lowest ids and make their pieces
+            // before they wait for anything; the bound only guards against a
+            // broken dispatch-order assumption.  Each wave looks for itself.
+            unsigned spins = 0;
+            while ((int)(__builtin_amdgcn_readfirstlane(poll_u32(a.tflag)) - a.t_target) < 0 && ++spins < (1u << 26))
+                __builtin_amdgcn_s_sleep(2);
+            load_t(tl0, 0, 0);
+        }
+        for (int h = 0; h < a.r_pad / 64; ++h) {
+            u32x4 af[2][WNF];
+            if (h == 0) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int f = 0; f < WNF; ++f) af[c][f] = af0[c][f];
+            } else {
+                load_a(af, h);
+            }
+            // T over the K pieces in K order, rounded once to bf16.
+            f32x4 lo[2][MB], hi[2][MB];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int b = 0; b < MB; ++b) lo[c][b] = hi[c][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j0 = 0; j0 < a.t_splits; j0 += JB) {
+                f32x4 tl[2][MB][JB][2];
+                if (h == 0 && j0 == 0) {
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+#pragma unroll
+                        for (int b = 0; b < MB; ++b)
+#pragma unroll
+                            for (int u = 0; u < JB; ++u) {
+                                tl[c][b][u][0] = tl0[c][b][u][0];
+                                tl[c][b][u][1] = tl0[c][b][u][1];
+                            }
+                } else {
+                    load_t(tl, h, j0);
+                }
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int b = 0; b < MB; ++b)
+#pragma unroll
+                        for (int u = 0; u < JB; ++u) {
+                            lo[c][b] += tl[c][b][u][0];
+                            hi[c][b] += tl[c][b][u][1];
+                        }
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int b = 0; b < MB; ++b) {
+                    const u32x4 tf = u32x4{pack_bf16x2(lo[c][b][0], lo[c][b][1]), pack_bf16x2(lo[c][b][2], lo[c][b][3]),
+                                           pack_bf16x2(hi[c][b][0], hi[c][b][1]), pack_bf16x2(hi[c][b][2], hi[c][b][3])};
+#pragma unroll
+                    for (int f = 0; f < WNF; ++f) acc[f][b] = mfma16(af[c][f], tf, acc[f][b]);
+                }
+        }
+    }
+
+#pragma unroll
     for (int f = 0; f < WNF; ++f) {
         const int n = nw + f * 16 + 4 * g;
         if (n >= a.N) continue;
@@ -361,74 +501,78 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
             store_out(a, m, n, o);
         }
     }
-    if (a.splits > 1 && tid == 0) __hip_atomic_store(&a.counters[tn], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.splits > 1 && tid == 0) __hip_atomic_store(&a.cnt[tn], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MB, int RT, int NSTEPS>
-hipError_t launch_sk(const SArgs &a, int tiles_n, hipStream_t s) {
-    hipLaunchKernelGGL((skinny_kernel<MB, RT, NSTEPS>), dim3(tiles_n, a.splits), dim3(SNT), 0, s, a);
-    return hipGetLastError();
+template <int MB, int NSTEPS>
+hipError_t launch_sk(const SArgs &a, hipStream_t s) {
+    if constexpr (x_lds_bytes<MB, NSTEPS>() + 4 * MB * 64 * 16 + 64 > LDS_MAX) {
+        return hipErrorInvalidValue;
+    } else {
+        const int grid = a.tiles_n * a.splits;
+        hipLaunchKernelGGL((skinny_kernel<MB, NSTEPS>), dim3(grid), dim3(SNT), 0, s, a);
+        return hipGetLastError();
+    }
 }
 
-template <int MB, int RT>
-hipError_t launch_sk_steps(const SArgs &a, int tiles_n, hipStream_t s) {
-    switch (a.k_slice / 64) {
-        case 4: return launch_sk<MB, RT, 4>(a, tiles_n, s);
-        case 8: return launch_sk<MB, RT, 8>(a, tiles_n, s);
-        case 16: return launch_sk<MB, RT, 16>(a, tiles_n, s);
+template <int MB>
+hipError_t launch_sk_steps(int k_slice, const SArgs &a, hipStream_t s) {
+    switch (k_slice / 64) {
+        case 8: return launch_sk<MB, 8>(a, s);
+        case 16: return launch_sk<MB, 16>(a, s);
+        case 32: return launch_sk<MB, 32>(a, s);
+        case 64: return launch_sk<MB, 64>(a, s);
     }
     return hipErrorInvalidValue;
 }
 
-// Row blocks (MB) x rank fragments per wave (RT) that are instantiated: the
-// register budget allows RT <= 8 / MB (larger combinations would spill).
-hipError_t launch_sk_m(const SArgs &a, int tiles_n, hipStream_t s) {
-    const int rt = (a.r_pad + 63) / 64;
-    if (a.M <= 16) {
-        if (rt <= 1) return launch_sk_steps<1, 1>(a, tiles_n, s);
-        if (rt <= 2) return launch_sk_steps<1, 2>(a, tiles_n, s);
-        if (rt <= 4) return launch_sk_steps<1, 4>(a, tiles_n, s);
-        if (rt <= 8) return launch_sk_steps<1, 8>(a, tiles_n, s);
-    } else if (a.M <= 32) {
-        if (rt <= 1) return launch_sk_steps<2, 1>(a, tiles_n, s);
-        if (rt <= 2) return launch_sk_steps<2, 2>(a, tiles_n, s);
-        if (rt <= 4) return launch_sk_steps<2, 4>(a, tiles_n, s);
-    } else if (a.M <= SMAX_M) {
-        if (rt <= 1) return launch_sk_steps<4, 1>(a, tiles_n, s);
-        if (rt <= 2) return launch_sk_steps<4, 2>(a, tiles_n, s);
-    }
-    return hipErrorInvalidValue;
-}
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-int skinny_col_tile() { return SBN; }
+bool skinny_supports(int64_t M) { return M >= 1 && M <= SMAX_M; }
 
-bool skinny_supports(int64_t M, int64_t r_pad) {
-    const int64_t rt = (r_pad + 63) / 64;
-    if (M <= 16) return rt <= 8;
-    if (M <= 32) return rt <= 4;
-    if (M <= SMAX_M) return rt <= 2;
-    return false;
+SkinnyPlan skinny_plan(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t splits_hint) {
+    SkinnyPlan pl{};
+    pl.mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    pl.tiles_n = (int)cdiv64(N, SBN);
+    // K slice (512 to 4096 elements): the x slice of 16 mb rows must fit in
+    // LDS, and about one work-group per CU (or the hinted number of slices)
+    // is wanted.
+    const int64_t max_ks = 4096 / pl.mb;
+    const int64_t want = splits_hint > 0 ? splits_hint : cdiv64(256, pl.tiles_n);
+    const int64_t need = cdiv64(K, want < 1 ? 1 : want);
+    int64_t ks = 512;
+    while (ks < need && ks < max_ks) ks *= 2;
+    pl.k_slice = (int)ks;
+    pl.splits = (int)cdiv64(K, ks);
+    // T pieces: 16 ranks over KP elements of a slice each (KP = 4 x 256, or
+    // the whole slice when that is shorter); the first pwg work-groups of
+    // every slice compute them.
+    pl.groups = (int)(r_pad / 16);
+    const int64_t kp = ks < 1024 ? ks : 1024;
+    pl.t_kslice = (int)kp;
+    pl.pps = (int)(pl.groups * (ks / kp));
+    pl.pwg = pl.pps < pl.tiles_n ? pl.pps : pl.tiles_n;
+    pl.t_splits = (int)(pl.splits * (ks / kp));
+    pl.producers = r_pad > 0 ? pl.pwg * pl.splits : 0;  // work-groups that compute pieces
+    return pl;
 }
 
-bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t splits) {
+int64_t skinny_sync_words(const SkinnyPlan &pl) { return (int64_t)pl.tiles_n + 1; }
+
+bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, const SkinnyPlan &pl) {
     // Every buffer descriptor must stay below 2^31 bytes.
     const int64_t lim = (int64_t)1 << 31;
+    // The piece work-groups must all be resident at once (at most one per CU).
     return (int64_t)SBN * K < lim && M * K * 2 < lim && r_pad * K * 2 < lim && (int64_t)SBN * r_pad * 2 < lim &&
-           splits * M * N * 4 < lim && N * 2 < lim;
-}
-
-int skinny_slice_steps(int64_t K, int64_t N, int64_t splits_hint) {
-    const int64_t tiles_n = (N + SBN - 1) / SBN;
-    const int64_t ksteps = (K + 63) / 64;
-    int64_t want = splits_hint > 0 ? splits_hint : (256 + tiles_n - 1) / tiles_n;  // ~one work-group per CU
-    if (want < 1) want = 1;
-    const int64_t per = (ksteps + want - 1) / want;
-    return per <= 4 ? 4 : (per <= 8 ? 8 : 16);
+           (int64_t)pl.splits * M * N * 4 < lim && (int64_t)pl.t_splits * M * r_pad * 4 < lim && N * 2 < lim &&
+           K < lim && (int64_t)pl.tiles_n * pl.splits < lim && pl.producers <= 256;
 }
 
 hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t s) {
+    const SkinnyPlan &pl = p.plan;
+    if (!p.sync || (pl.splits > 1 && !p.partials) || (p.r > 0 && !p.t_part)) return hipErrorInvalidValue;
     SArgs a{};
     a.x = (const unsigned char *)p.x;
     a.B = (const unsigned char *)p.B;
@@ -437,7 +581,7 @@ hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t 
     a.bias = (const unsigned char *)p.bias;
     a.y = p.y;
     a.partials = p.partials;
-    a.counters = p.counters;
+    a.tpart = p.t_part;
     a.scale = p.scale;
     a.M = (int)p.M;
     a.K = (int)p.K;
@@ -445,12 +589,22 @@ hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t 
     a.r = (int)p.r;
     a.r_pad = (int)p.r_pad;
     a.lda = a_eff == p.A ? (int)p.r : (int)p.r_pad;
-    a.k_slice = (int)p.k_slice;
-    a.splits = p.splits;
+    a.splits = pl.splits;
+    a.tiles_n = pl.tiles_n;
+    a.t_splits = pl.t_splits;
+    a.pps = pl.pps;
+    a.pwg = p.r > 0 ? pl.pwg : 0;
+    a.cnt = p.sync;
+    a.tflag = p.sync + pl.tiles_n;
+    a.t_target = p.t_target;
     a.y_vec = (p.N % 4 == 0) && ((uintptr_t)p.y % 16 == 0) && ((uintptr_t)p.partials % 16 == 0);
     a.out_f32 = p.out_f32;
-    const int tiles_n = (int)((p.N + SBN - 1) / SBN);
-    return launch_sk_m(a, tiles_n, s);
+    switch (pl.mb) {
+        case 1: return launch_sk_steps<1>(pl.k_slice, a, s);
+        case 2: return launch_sk_steps<2>(pl.k_slice, a, s);
+        case 4: return launch_sk_steps<4>(pl.k_slice, a, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace ll

@@ -141,6 +141,46 @@ def test_random_parity(dev, shape, out_f32):
         parity.check(y, y_ref, out_f32)
 
 
+@pytest.mark.parametrize("t_splits", [1, 2, 3, 5, 0])
+def test_tiled_t_split_counts(dev, t_splits):
+    """T = x B^T summed over K slices: same gates, and repeat calls agree bit
+    for bit (the slice counters are back at zero, the sum order is fixed)."""
+    d = wl.random_inputs(300, 1280, 520, 80, seed=17)
+    y_ref = oracle_y(d)
+    say("tiled t_splits", t_splits)
+    h = make_handle(dev, Path.TILED)
+    h.set_option(Option.T_SPLITS, t_splits)
+    g = to_dev(d, dev)
+    y1 = run(h, g)
+    y2 = run(h, g)
+    assert torch.equal(y1, y2)
+    parity.check(parity.to_f64(y1), y_ref, False)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
+def test_handle_reuse_across_shapes(dev, path):
+    """One handle, a sequence of shapes that change the column-tile count,
+    the row-tile count, the rank (and so the T flag step), with r = 0 calls
+    in between: every call must match the oracle (the handle's counters
+    are restarted whenever their layout changes)."""
+    if path == Path.SKINNY:
+        shapes = [(16, 512, 256, 64), (16, 512, 1024, 64), (16, 512, 1024, 0), (16, 512, 256, 64),
+                  (16, 512, 256, 128), (9, 1024, 2176, 64), (16, 512, 256, 64)]
+    else:
+        shapes = [(300, 256, 512, 64), (600, 256, 512, 64), (300, 256, 512, 128), (300, 256, 512, 0),
+                  (300, 256, 512, 64), (700, 512, 384, 192), (300, 256, 512, 64)]
+    h = make_handle(dev, path)
+    cache = {}
+    for rep in range(2):
+        for i, (M, K, N, r) in enumerate(shapes):
+            say("reuse", path.name, rep, (M, K, N, r))
+            if (M, K, N, r) not in cache:
+                d = wl.random_inputs(M, K, N, r, seed=40 + i)
+                cache[(M, K, N, r)] = (d, oracle_y(d), to_dev(d, dev))
+            d, y_ref, g = cache[(M, K, N, r)]
+            parity.check(parity.to_f64(run(h, g)), y_ref, False)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 32])
 def test_skinny_split_counts(dev, splits):
     d = wl.random_inputs(16, 2048, 640, 64, seed=7)
@@ -297,6 +337,11 @@ def test_bad_arguments_return_status(dev):
         d2 = to_dev(wl.random_inputs(65, 64, 32, 4, seed=13), dev)
         h.forward(d2["x"], d2["A"], d2["B"], d2["Q"], d2["scale"], d2["bias"])
     assert e.value.status == Status.UNSUPPORTED
+    for key, bad in ((Option.PATH, 3), (Option.OUTPUT_F32, 2), (Option.SPLIT_K, -1), (Option.PROFILE, 5),
+                     (Option.T_SPLITS, 65), (Option.T_SPLITS, -1), (99, 0)):
+        with pytest.raises(LiteLinearError) as e:
+            h.set_option(key, bad)
+        assert e.value.status == Status.INVALID_ARG
 
 
 def test_profiling_counts_launches(dev):
