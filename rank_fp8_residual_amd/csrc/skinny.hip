@@ -297,10 +297,12 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
         wait_vmcnt<0>();
         __syncthreads();
         if (tid == 0) {
-            // The first look at the T flag rides along with the counter.
-            const unsigned last = bump_u32(&a.cnt[tn]) == (unsigned)(a.splits - 1) ? 1u : 0u;
-            tflag_sh = a.r > 0 ? poll_u32(a.tflag) : 0u;
-            is_last = last;
+            // The first look at the T flag goes out together with the counter
+            // update (neither waits for the other).
+            const unsigned tf = poll_u32(a.tflag);
+            const unsigned old = bump_u32(&a.cnt[tn]);
+            tflag_sh = tf;
+            is_last = old == (unsigned)(a.splits - 1) ? 1u : 0u;
         }
         __syncthreads();
         if (!is_last) return;
@@ -313,7 +315,7 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
         a.splits > 1 ? tflag_sh : (a.r > 0 ? __builtin_amdgcn_readfirstlane(poll_u32(a.tflag)) : 0u);
     bool t_ready = a.r <= 0 || (int)(tflag0 - a.t_target) >= 0;
 
-    constexpr int SB = (32 / (WNF * MB)) > 0 ? 32 / (WNF * MB) : 1;  // slices per batch of loads
+    constexpr int SB = 4;  // slices per batch of loads
     const unsigned pstride = (unsigned)a.M * (unsigned)a.N * 4u;
     auto load_batch = [&](f32x4 (&p)[SB][WNF][MB], int s0) {
 #pragma unroll
