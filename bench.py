@@ -2,7 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload dit_r64] [--gpus 1]
 
-One step is one litelinear_forward (all kernels of the path) over one batch
+One step is one litelinear_forward (every kernel of the path) over one batch
 of seeded synthetic inputs already resident in HBM.  Several copies of the
 inputs and outputs are rotated so that the working set exceeds the 256 MB
 Infinity Cache and every step reads its operands from HBM.
@@ -12,14 +12,22 @@ Prints ONE JSON line with:
                     (2 M (in out + r in + r out) flops per step);
   roofline          the dominant kernel's achieved rate against the MI355X
                     peak for its bound (dense bf16 matrix cores, 2.5 PFLOP/s,
-                    or HBM, 8 TB/s), from HIP events recorded on the launch
-                    stream around every launch of that kernel;
+                    or HBM, 8 TB/s): algorithmic work per launch over the
+                    kernel's time per launch, from HIP events on the launch
+                    stream around the timed region (or, when a step launches
+                    more than one kernel, around every launch of that one);
+                    `traffic` is the kernel's measured HBM bytes per launch
+                    when a counter record for the current kernel sources is
+                    committed under profiles/ (else null);
   cpu_baseline      the float64 CPU oracle timed on a sample of rows of the
-                    same workload, on this host's cores.
+                    same workload, on this host's cores;
+  workloads         a shorter measurement of every other workload.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import math
 import os
@@ -33,6 +41,9 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth
 MALL_BYTES = 256 << 20      # Infinity Cache
+COPY_PROBE_BYTES = 256 << 20
+KERNEL_NAMES = {"main": "fused_kernel", "pad_a": "pad_rows_kernel", "skinny": "skinny_kernel"}
+HEADLINE = "dit_r64"
 
 
 def log(*a):
@@ -42,13 +53,16 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="dit_r64")
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=300)
+    p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--copies", type=int, default=0, help="rotating input/output copies (0: auto)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-summary", action="store_true", help="skip the other workloads")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a plain 256 MiB device copy (reference kernel for HBM counters)")
     p.add_argument("--path", default="auto", choices=["auto", "skinny", "tiled"])
     p.add_argument("--split-k", type=int, default=0, help="skinny path: K-slice hint (0: automatic)")
     p.add_argument("--t-splits", type=int, default=0, help="tiled path: K slices per T block (0: automatic)")
@@ -58,14 +72,152 @@ def parse():
 def kernel_flops_bytes(w, kernel: str):
     """Algorithmic flops and bytes one launch of `kernel` is charged with.
 
-    Both the tiled kernel and the skinny kernel compute the whole forward in
+    The tiled kernel and the skinny kernel each compute the whole forward in
     one launch: 2 M (in out + r in + r out) flops, and every input read once
-    plus y written once.  The A-padding copy (ranks not a multiple of 8) moves
-    2 out r bytes in and 2 out r_pad bytes out."""
+    plus y written once.  The A-padding copy (ranks not a multiple of 8)
+    moves 2 out r bytes in and 2 out r_pad bytes out."""
     if kernel == "pad_a":
         r_pad = -(-w.rank // 64) * 64
         return 0, 2 * w.out_features * (w.rank + r_pad)
     return w.flops, w.bytes
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources: a counter record applies only to them."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "rank_fp8_residual_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel: str, workload: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel sources."""
+    digest = source_digest()
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(f):
+            if not line.startswith("traffic-record:"):
+                continue
+            try:
+                rec = json.loads(line.split(":", 1)[1])
+            except ValueError:
+                continue
+            if rec.get("kernel") == kernel and rec.get("workload") == workload and rec.get("sources") == digest:
+                return rec
+    return None
+
+
+class Runner:
+    """Rotating resident copies of one workload's inputs and a handle."""
+
+    def __init__(self, w, args, dev, copies=0):
+        import torch
+
+        from rank_fp8_residual_amd import Handle, Option, Path
+        from rank_fp8_residual_amd import workloads as wl
+
+        self.w = w
+        t0 = time.time()
+        self.d = wl.make_inputs(w, seed=args.seed)
+        log(f"{w.name}: inputs drawn in {time.time() - t0:.1f}s")
+        self.copies = copies or max(2, min(64, math.ceil(4 * MALL_BYTES / w.bytes)))
+        self.sets = []
+        for _ in range(self.copies):
+            g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in self.d.items()}
+            g["y"] = torch.empty((w.M, w.out_features), dtype=torch.bfloat16, device=dev)
+            self.sets.append(g)
+        torch.cuda.synchronize()
+        self.h = Handle(dev.index)
+        self.h.set_option(Option.PATH, {"auto": Path.AUTO, "skinny": Path.SKINNY, "tiled": Path.TILED}[args.path])
+        self.h.set_option(Option.SPLIT_K, args.split_k)
+        self.h.set_option(Option.T_SPLITS, args.t_splits)
+        self.dev = dev
+
+    def step(self, i):
+        g = self.sets[i % self.copies]
+        self.h.forward(g["x"], g["A"], g["B"], g["Q"], g["scale"], g["bias"], out=g["y"])
+
+    def timed(self, warmup, steps):
+        """Warm up, then time exactly `steps` steps: ms per step."""
+        import torch
+
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(self.dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            self.step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def step_spread(self, steps):
+        """p10 / p50 / p90 of single-step times (an event pair per step)."""
+        import torch
+
+        stream = torch.cuda.current_stream(self.dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            self.step(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        q = lambda f: round(t[min(len(t) - 1, int(f * len(t)))] * 1e3, 2)
+        return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "unit": "us"}
+
+    def kernel_times(self, steps):
+        """Average duration per launch of each kernel kind (library events)."""
+        import torch
+
+        from rank_fp8_residual_amd import Kernel, Option
+
+        self.h.set_option(Option.PROFILE, 1)
+        for i in range(steps):
+            self.step(i)
+        torch.cuda.synchronize()
+        kt = {}
+        for name, kind in (("pad_a", Kernel.PAD_A), ("main", Kernel.MAIN), ("skinny", Kernel.SKINNY)):
+            ms, n = self.h.kernel_time(kind, reset=True)
+            if n:
+                kt[name] = ms / n
+        self.h.set_option(Option.PROFILE, 0)
+        return kt
+
+    def release(self):
+        import torch
+
+        self.sets = []
+        torch.cuda.empty_cache()
+
+
+def roofline(w, kt, ms_step):
+    """Roofline of the dominant kernel.  Its duration per launch is the timed
+    region's time per step when the step launches that kernel alone (events
+    bracketing back-to-back launches, as a profiler's trace sees them), else
+    the library's per-launch event pairs."""
+    dom = max(kt, key=kt.get)
+    fl, by = kernel_flops_bytes(w, dom)
+    dur_s = (ms_step if len(kt) == 1 else kt[dom]) * 1e-3
+    if fl and fl / by > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(fl / dur_s / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(by / dur_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    rec = traffic_record(KERNEL_NAMES[dom], w.name)
+    roof["traffic"] = rec["hbm_bytes"] if rec else None
+    if rec:
+        roof["traffic_detail"] = {k: rec[k] for k in ("fetch_bytes", "write_bytes", "scale", "profile") if k in rec}
+    roof["kernel"] = KERNEL_NAMES[dom]
+    roof["kernel_us"] = round(dur_s * 1e6, 2)
+    roof["kernel_us_event_pairs"] = {k: round(v * 1e3, 2) for k, v in kt.items()}
+    roof["algorithmic"] = {"flops": fl, "bytes": by}
+    return roof
 
 
 def main():
@@ -77,10 +229,8 @@ def main():
               "so N GPUs give N times this figure)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from rank_fp8_residual_amd import Handle, Kernel, Option, Path
     from rank_fp8_residual_amd import workloads as wl
 
     if not torch.cuda.is_available():
@@ -89,82 +239,50 @@ def main():
     dev = torch.device("cuda", 0)
     w = wl.WORKLOADS[args.workload]
     log("workload", w)
-    t0 = time.time()
-    d = wl.make_inputs(w, seed=args.seed)
-    log(f"inputs drawn in {time.time() - t0:.1f}s")
+    run = Runner(w, args, dev, args.copies)
+    log(f"{run.copies} rotating copies resident ({run.copies * w.bytes / 2**20:.0f} MiB)")
 
-    per_copy = w.bytes
-    copies = args.copies or max(2, min(64, math.ceil(4 * MALL_BYTES / per_copy)))
-    sets = []
-    for c in range(copies):
-        g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
-        g["y"] = torch.empty((w.M, w.out_features), dtype=torch.bfloat16, device=dev)
-        sets.append(g)
-    torch.cuda.synchronize()
-    log(f"{copies} rotating copies resident ({copies * per_copy / 2**20:.0f} MiB)")
-
-    h = Handle(0)
-    h.set_option(Option.PATH, {"auto": Path.AUTO, "skinny": Path.SKINNY, "tiled": Path.TILED}[args.path])
-    h.set_option(Option.SPLIT_K, args.split_k)
-    h.set_option(Option.T_SPLITS, args.t_splits)
-
-    def step(i):
-        g = sets[i % copies]
-        h.forward(g["x"], g["A"], g["B"], g["Q"], g["scale"], g["bias"], out=g["y"])
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} done")
-
-    stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / args.steps
+    ms_step = run.timed(args.warmup, args.steps)
     tflops = w.flops / (ms_step * 1e-3) / 1e12
     gbs = w.bytes / (ms_step * 1e-3) / 1e9
     log(f"timed {args.steps} steps: {ms_step * 1e3:.2f} us/step, {tflops:.1f} TFLOP/s, {gbs:.0f} GB/s")
-
-    # Per-kernel times: HIP events the library records on the launch stream.
-    h.set_option(Option.PROFILE, 1)
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    kt = {}
-    for name, kind in (("pad_a", Kernel.PAD_A), ("main", Kernel.MAIN), ("skinny", Kernel.SKINNY)):
-        ms, n = h.kernel_time(kind, reset=True)
-        if n:
-            kt[name] = ms / n
-    h.set_option(Option.PROFILE, 0)
-    dom = max(kt, key=kt.get)
-    fl, by = kernel_flops_bytes(w, dom)
-    dur_s = kt[dom] * 1e-3
-    ai = fl / by
-    if ai > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        roof = {"bound": "mfma", "achieved": round(fl / dur_s / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": round(by / dur_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
-    roof["kernel"] = {"main": "fused_kernel (tiled path)", "pad_a": "pad_rows_kernel",
-                      "skinny": "skinny_kernel"}[dom]
-    roof["kernel_us"] = {k: round(v * 1e3, 2) for k, v in kt.items()}
-    log("per-kernel us", roof["kernel_us"])
+    spread = run.step_spread(min(args.steps, 200))
+    kt = run.kernel_times(args.steps)
+    roof = roofline(w, kt, ms_step)
+    log("kernel us", roof["kernel_us"], "event pairs", roof["kernel_us_event_pairs"], "traffic", roof["traffic"])
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, d, sets[0], args.cpu_seconds)
+        cpu = cpu_baseline(w, run.d, run.sets[0], args.cpu_seconds)
+    run.release()
+
+    summary = None
+    if not args.no_summary:
+        summary = {}
+        for name, wo in wl.WORKLOADS.items():
+            if name == w.name:
+                continue
+            r = Runner(wo, args, dev)
+            steps = 20 if wo.flops > 1e12 else 100
+            ms = r.timed(max(20, steps // 2), steps)
+            k = r.kernel_times(steps)
+            ro = roofline(wo, k, ms)
+            summary[name] = {
+                "M": wo.M, "in": wo.in_features, "out": wo.out_features, "r": wo.rank,
+                "us_per_step": round(ms * 1e3, 2),
+                "TFLOP/s": round(wo.flops / (ms * 1e-3) / 1e12, 2),
+                "GB/s": round(wo.bytes / (ms * 1e-3) / 1e9, 1),
+                "roofline": {k2: ro[k2] for k2 in ("bound", "achieved", "unit", "frac", "kernel", "traffic")},
+            }
+            log(name, summary[name])
+            r.release()
+
+    if args.copy_probe:
+        copy_probe(dev)
 
     line = {
         "metric": "fused LiteLinear TFLOP/s and HBM GB/s vs roofline, M=3630 in=2048 out=8192 r=64"
-        if args.workload == "dit_r64" else f"fused LiteLinear TFLOP/s and HBM GB/s vs roofline, {args.workload}",
+        if args.workload == HEADLINE else f"fused LiteLinear TFLOP/s and HBM GB/s vs roofline, {args.workload}",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -180,15 +298,31 @@ def main():
             "workload": f"{w.name}: M={w.M} in={w.in_features} out={w.out_features} r={w.rank}; "
                         "x/A/B/bias bf16, Q e4m3fn with per-tensor scale, y bf16",
             "M": w.M, "in": w.in_features, "out": w.out_features, "r": w.rank,
-            "rotating_copies": copies, "hbm_GBps": round(gbs, 1),
+            "rotating_copies": run.copies, "hbm_GBps": round(gbs, 1),
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
             "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "flops_per_step": w.flops, "bytes_per_step": w.bytes,
+            "step_us": spread,
         },
         "roofline": roof,
         "cpu_baseline": cpu,
+        "workloads": summary,
     }
     print(json.dumps(line), flush=True)
+
+
+def copy_probe(dev, reps=5):
+    """A plain device copy of COPY_PROBE_BYTES: under a counter run its
+    FETCH_SIZE / WRITE_SIZE per dispatch give the scale of those counters
+    (expected COPY_PROBE_BYTES each way)."""
+    import torch
+
+    src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: {reps} copies of {COPY_PROBE_BYTES} bytes")
 
 
 def cpu_baseline(w, d, g, target_s):
