@@ -374,13 +374,13 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
         // The ready counters of every row tile must have grown by the same
         // step in every launch so far; a different row-tile count or step
         // starts them again from zero (ordered on the stream).
-        const uint64_t key = ((uint64_t)ll::tiled_row_tiles(p, mc) << 32) | ll::tiled_flag_step(p);
+        const uint64_t key = ((uint64_t)ll::tiled_row_tiles(p, mc) << 32) | ll::tiled_flag_step(p, mc);
         if (key != h->tiled_key) {
             if (hipMemsetAsync(h->tile_sync, 0, h->tile_sync_bytes, stream) != hipSuccess) return LITELINEAR_ERR_HIP;
             h->tiled_key = key;
             h->tiled_epoch = 0;
         }
-        p.t_target = (h->tiled_epoch + 1u) * ll::tiled_flag_step(p);
+        p.t_target = (h->tiled_epoch + 1u) * ll::tiled_flag_step(p, mc);
     }
     st = timed_launch(h, LITELINEAR_KERNEL_MAIN, stream,
                       [&] { return ll::launch_tiled(p, mc, a_eff, h->tile_sync, stream); });

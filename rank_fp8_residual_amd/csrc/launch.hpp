@@ -36,8 +36,8 @@ bool a_needs_padding(int64_t r, const void *A);
 bool tiled_shape_ok(const TiledProblem &p, TileCfg c);
 int tiled_row_tiles(const TiledProblem &p, TileCfg c);
 hipError_t launch_pad_a(const void *A, void *a_pad, int64_t N, int64_t r, int64_t r_pad, hipStream_t s);
-// K slices per 64-column block of T: T is computed by tiled_row_tiles() x
-// (r_pad / 64) x t_splits producer work-groups, enough of them to finish
+// K slices per block of T: T is computed by tiled_row_tiles() x
+// (r_pad / tiled_t_cols()) x t_splits producer work-groups, enough of them to finish
 // early but few enough to leave most CUs to the output tiles.
 // hint > 0 asks for that many slices (capped at the number of K steps).
 int tiled_t_splits(const TiledProblem &p, TileCfg c, int64_t hint);
@@ -47,7 +47,10 @@ int tiled_t_splits(const TiledProblem &p, TileCfg c, int64_t hint);
 // counters were zeroed) sets t_target = e * tiled_flag_step() (mod 2^32).
 // Per T block, finished K slices (left at zero by every launch).
 int64_t tiled_sync_words(const TiledProblem &p, TileCfg c);
-unsigned tiled_flag_step(const TiledProblem &p);
+unsigned tiled_flag_step(const TiledProblem &p, TileCfg c);
+// Columns of T per producer block (64, or 256 for ranks that are multiples
+// of 256 with 256-wide output tiles).
+int tiled_t_cols(const TiledProblem &p, TileCfg c);
 hipError_t launch_tiled(const TiledProblem &p, TileCfg c, const void *a_eff, unsigned *sync, hipStream_t s);
 
 // Skinny path (M <= 64): T producers plus output work-groups of 128
