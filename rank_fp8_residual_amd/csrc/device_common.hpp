@@ -41,21 +41,20 @@ __device__ __forceinline__ void fp8x16_to_bf16x16(u32x4 q, u32x4 &h0, u32x4 &h1)
     h1 = u32x4{c.x, c.y, d.x, d.y};
 }
 
-// float32 -> bf16 bits, round to nearest even (NaN kept quiet).
+// float32 -> bf16 bits, round to nearest even: gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32) under the default rounding mode.
 __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
-    unsigned u = __builtin_bit_cast(unsigned, f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
-        return (unsigned short)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (unsigned short)(u >> 16);
+    return __builtin_bit_cast(unsigned short, (__bf16)f);
 }
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short h) {
     return __builtin_bit_cast(float, (unsigned)h << 16);
 }
 
+// Two floats -> two bf16 (round to nearest even) in one dword, a low.
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-    return (unsigned)f32_to_bf16_rne(a) | ((unsigned)f32_to_bf16_rne(b) << 16);
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(unsigned, v);
 }
 
 __device__ __forceinline__ u32x4 load16(const void *p) {

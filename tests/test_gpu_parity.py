@@ -158,6 +158,49 @@ def test_tiled_t_split_counts(dev, t_splits):
 
 
 @pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
+def test_bf16_output_is_rne_of_f32_output(dev, path):
+    """The bf16 output is the float32 output rounded to nearest even (the
+    kernels accumulate identically in both modes; only the final store
+    differs), checked element by element, including values placed exactly
+    halfway between bf16 neighbours, subnormal-range and huge results."""
+    M = 48 if path == Path.SKINNY else 300
+    d = wl.random_inputs(M, 512, 640, 32, seed=71)
+    g = to_dev(d, dev)
+    say("bf16 rounding", path.name)
+    y32 = run(make_handle(dev, path, out_f32=True), g)
+    y16 = run(make_handle(dev, path), g)
+    assert torch.equal(y32.to(torch.bfloat16), y16)
+    # halfway cases: scale the same inputs by powers of two so results span the
+    # bf16 range, and use exact inputs whose sums land on ties
+    for sc in (2.0 ** -120, 2.0 ** 100):
+        g2 = dict(g, scale=g["scale"] * sc, A=g["A"] * 0, bias=None)
+        y32 = run(make_handle(dev, path, out_f32=True), g2)
+        y16 = run(make_handle(dev, path), g2)
+        assert torch.equal(y32.to(torch.bfloat16), y16), sc
+    de = wl.exact_inputs(M, 512, 640, 16, seed=72)
+    ge = to_dev(de, dev)
+    y32 = run(make_handle(dev, path, out_f32=True), ge)
+    y16 = run(make_handle(dev, path), ge)
+    assert torch.equal(y32.to(torch.bfloat16), y16)
+
+
+@pytest.mark.parametrize("r", [256, 512, 320])
+def test_wide_t_blocks(dev, r):
+    """Ranks that are multiples of 256 on 256 x 256 output tiles take T in
+    256-column producer blocks (320 does not, for comparison); sampled rows
+    against the oracle, bf16 and float32 output."""
+    M, K, N = 4096, 512, 4096
+    d = wl.random_inputs(M, K, N, r, seed=60 + r)
+    g = to_dev(d, dev)
+    rows = sample_rows(M, 40)
+    y_ref = oracle_y(d, rows=rows)
+    for out_f32 in (False, True):
+        say("wide T blocks", r, "f32" if out_f32 else "bf16")
+        y = run(make_handle(dev, Path.TILED, out_f32), g)
+        parity.check(parity.to_f64(y[torch.from_numpy(rows).to(dev)]), y_ref, out_f32)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
 def test_handle_reuse_across_shapes(dev, path):
     """One handle, a sequence of shapes that change the column-tile count,
     the row-tile count, the rank (and so the T flag step), with r = 0 calls
