@@ -144,4 +144,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Work-group barrier without a memory fence (loads may stay in flight).
 __device__ __forceinline__ void barrier_nofence() { __builtin_amdgcn_s_barrier(); }
 
+// The same barrier, also a compiler barrier for memory accesses: LDS reads
+// written after it are not moved above it (the s_barrier intrinsic alone
+// orders no memory access), and no wait for loads in flight is added (a
+// fence would wait for every load that writes LDS).
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace ll
