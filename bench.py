@@ -264,7 +264,7 @@ def main():
                 continue
             r = Runner(wo, args, dev)
             steps = 20 if wo.flops > 1e12 else 100
-            ms = r.timed(max(20, steps // 2), steps)
+            ms = r.timed(20 if wo.flops > 1e12 else 300, steps)
             k = r.kernel_times(steps)
             ro = roofline(wo, k, ms)
             summary[name] = {
