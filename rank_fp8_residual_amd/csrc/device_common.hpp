@@ -153,4 +153,13 @@ __device__ __forceinline__ void barrier_lds() {
     asm volatile("" ::: "memory");
 }
 
+// barrier_lds after this wave's own LDS reads and writes have completed
+// (lgkmcnt 0): LDS written before it by any wave is what reads after it see.
+__device__ __forceinline__ void barrier_lds_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left open
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace ll

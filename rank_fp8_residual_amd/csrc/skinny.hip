@@ -136,6 +136,24 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) bv[f][v] = bload_bf16(rb, (unsigned)(nw + 16 * f + 4 * g + v));
 
+    // The first 64 ranks of this lane's A rows, also requested up front: A is
+    // read from HBM for the first time, and only a final work-group (any
+    // work-group may be one) uses it, after its Q stream.
+    const rsrc_t ra = make_rsrc(a.A + (int64_t)n0 * a.lda * 2, (int64_t)rows_n * a.lda * 2);
+    auto load_a = [&](u32x4 (&af)[2][WNF], int h) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int f = 0; f < WNF; ++f) {
+                const int ka = 64 * h + 32 * c + 8 * g;
+                af[c][f] = bload16(ra, ((unsigned)(wave * (WNF * 16) + 16 * f + l16) * (unsigned)a.lda + (unsigned)ka) *
+                                               2u +
+                                           (ka < a.lda ? 0u : kOOB));
+            }
+    };
+    u32x4 af0[2][WNF];
+    if (a.r > 0) load_a(af0, 0);
+
     // x[:, kb : kb + KS] -> LDS, rows of XS bytes (the padding puts the 16
     // rows a fragment read touches on distinct banks).  One instruction
     // moves 1 KB (512 elements) of one row; instruction i goes to wave i % 4.
@@ -190,14 +208,7 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
     // device-coherent as float32 piece [slice (KS / KP) + p / nfrag][f][m][16].
     if (has_piece) {
         const rsrc_t rtp = make_rsrc(a.tpart, (int64_t)a.t_splits * nfrag * a.M * 16 * 4);
-        for (int p = tn; p < a.pps; p += a.pwg) {
-            u32x4 bb[KW / 32];
-            if (p == tn) {
-#pragma unroll
-                for (int s2 = 0; s2 < KW / 32; ++s2) bb[s2] = bfirst[s2];
-            } else {
-                load_b(bb, p);
-            }
+        auto piece = [&](const u32x4 (&bb)[KW / 32], int p) {
             const int f = p % nfrag, q = p / nfrag;
             f32x4 tacc[MB];
 #pragma unroll
@@ -228,6 +239,15 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
                 }
             }
             __syncthreads();
+        };
+        // The first piece's B rows are the registers loaded before the Q
+        // loads (this code path waits for nothing newer); later pieces load
+        // their own.
+        piece(bfirst, tn);
+        for (int p = tn + a.pwg; p < a.pps; p += a.pwg) {
+            u32x4 bb[KW / 32];
+            load_b(bb, p);
+            piece(bb, p);
         }
     }
 
@@ -334,47 +354,32 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
     const bool vec_sum = a.splits > 1 && a.y_vec;
     if (vec_sum) load_batch(pb, 0);
 
-    // T A^T runs over the padded rank 64 at a time (two 32-rank chunks c).
-    // Lane holds A[n][64 h + 32 c + 8 g, +8) and, for T, the float32 pieces
-    // of ranks 8 (g % 2) .. +8 of fragment 4 h + 2 c + g / 2 of row
-    // m = 16 b + l16, JB K ranges per batch (ranges past the last read zero).
-    constexpr int JB = 8 / MB;
-    const rsrc_t ra = make_rsrc(a.A + (int64_t)n0 * a.lda * 2, (int64_t)rows_n * a.lda * 2);
+    // T A^T runs over the padded rank 64 at a time (group h, two 32-rank
+    // chunks c).  Lane holds A[n][64 h + 32 c + 8 g, +8) and, as bf16, T of
+    // ranks 8 (g % 2) .. +8 of fragment 4 h + 2 c + g / 2 of row
+    // m = 16 b + l16.  The float32 pieces of a group's four fragments are
+    // staged in LDS (over the x slice, no longer read), jc K ranges at a
+    // time, each read from memory once per work-group.
     const rsrc_t rtp = make_rsrc(a.tpart, (int64_t)a.t_splits * nfrag * a.M * 16 * 4);
-    auto load_a = [&](u32x4 (&af)[2][WNF], int h) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int f = 0; f < WNF; ++f) {
-                const int ka = 64 * h + 32 * c + 8 * g;
-                af[c][f] = bload16(ra, ((unsigned)(wave * (WNF * 16) + 16 * f + l16) * (unsigned)a.lda + (unsigned)ka) *
-                                               2u +
-                                           (ka < a.lda ? 0u : kOOB));
-            }
-    };
-    auto load_t = [&](f32x4 (&tl)[2][MB][JB][2], int h, int j0) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int frag = 4 * h + 2 * c + (g >> 1);
-#pragma unroll
-            for (int b = 0; b < MB; ++b) {
-                const int m = 16 * b + l16;
-#pragma unroll
-                for (int u = 0; u < JB; ++u) {
-                    const int j = j0 + u;
-                    const unsigned off = (unsigned)((((j * nfrag + frag) * a.M + m) * 16 + 8 * (g & 1)) * 4) +
-                                         (m < a.M && j < a.t_splits ? 0u : kOOB);
-                    tl[c][b][u][0] = bload16f_dc(rtp, off);
-                    tl[c][b][u][1] = bload16f_dc(rtp, off + 16u);
-                }
-            }
+    // A staged K range holds, for each of the 4 fragments, MB blocks of 64
+    // units of 16 bytes (one load instruction each): unit 4 m + i of a
+    // fragment is row m's ranks 4 i .. +4, units past 4 M read zero.
+    constexpr int JU = 4 * MB * 64;  // units per staged K range
+    const int jc = x_lds_bytes<MB, NSTEPS>() / (JU * 16);
+    auto stage_t = [&](int h, int j0) {
+        const int nj = a.t_splits - j0 < jc ? a.t_splits - j0 : jc;
+        for (int i = wave; i < nj * 4 * MB; i += 4) {
+            const int jj = i / (4 * MB), fr = (i / MB) % 4, k = i % MB, u = 64 * k + lane;
+            const bool ok = u < 4 * a.M && 4 * h + fr < nfrag;
+            const unsigned off = (unsigned)(((j0 + jj) * nfrag + 4 * h + fr) * a.M * 64 + u * 16) + (ok ? 0u : kOOB);
+            bload16_lds<kDeviceCoherent>(rtp, xs + 1024 * i, off);
         }
     };
-    u32x4 af0[2][WNF];
-    f32x4 tl0[2][MB][JB][2];
     if (a.r > 0) {
-        load_a(af0, 0);
-        if (t_ready) load_t(tl0, 0, 0);
+        // Every wave's last read of the x slice is behind it (with several
+        // slices the barrier before the counter update already says so).
+        if (a.splits <= 1) barrier_lds();
+        if (t_ready) stage_t(0, 0);
     }
 
     // Sum of the slices, each element in slice order from zero.
@@ -435,7 +440,7 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
             unsigned spins = 0;
             while ((int)(__builtin_amdgcn_readfirstlane(poll_u32(a.tflag)) - a.t_target) < 0 && ++spins < (1u << 26))
                 __builtin_amdgcn_s_sleep(2);
-            load_t(tl0, 0, 0);
+            stage_t(0, 0);
         }
         for (int h = 0; h < a.r_pad / 64; ++h) {
             u32x4 af[2][WNF];
@@ -447,46 +452,46 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
             } else {
                 load_a(af, h);
             }
-            // T over the K pieces in K order, rounded once to bf16.
-            f32x4 lo[2][MB], hi[2][MB];
+            // T over the K pieces in K order, rounded once to bf16: thread
+            // tid sums the units tid + 256 i of the staged ranges and writes
+            // them as bf16 to LDS (over `red`, same unit order), from where
+            // every wave reads its operand.
+            f32x4 ts[MB];
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int b = 0; b < MB; ++b) lo[c][b] = hi[c][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int j0 = 0; j0 < a.t_splits; j0 += JB) {
-                f32x4 tl[2][MB][JB][2];
-                if (h == 0 && j0 == 0) {
-#pragma unroll
-                    for (int c = 0; c < 2; ++c)
-#pragma unroll
-                        for (int b = 0; b < MB; ++b)
-#pragma unroll
-                            for (int u = 0; u < JB; ++u) {
-                                tl[c][b][u][0] = tl0[c][b][u][0];
-                                tl[c][b][u][1] = tl0[c][b][u][1];
-                            }
-                } else {
-                    load_t(tl, h, j0);
+            for (int i = 0; i < MB; ++i) ts[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j0 = 0; j0 < a.t_splits; j0 += jc) {
+                if (h > 0 || j0 > 0) {
+                    barrier_lds_sync();  // every wave is done with the previous ranges
+                    stage_t(h, j0);
                 }
+                wait_vmcnt<0>();
+                barrier_lds();
+                const int nj = a.t_splits - j0 < jc ? a.t_splits - j0 : jc;
+                for (int jj = 0; jj < nj; ++jj) {
 #pragma unroll
-                for (int c = 0; c < 2; ++c)
-#pragma unroll
-                    for (int b = 0; b < MB; ++b)
-#pragma unroll
-                        for (int u = 0; u < JB; ++u) {
-                            lo[c][b] += tl[c][b][u][0];
-                            hi[c][b] += tl[c][b][u][1];
-                        }
+                    for (int i = 0; i < MB; ++i)
+                        ts[i] += *reinterpret_cast<const f32x4 *>(xs + (jj * JU + tid + 256 * i) * 16);
+                }
             }
+            unsigned char *tb = reinterpret_cast<unsigned char *>(red);
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                *reinterpret_cast<u32x2 *>(tb + (tid + 256 * i) * 8) =
+                    u32x2{pack_bf16x2(ts[i][0], ts[i][1]), pack_bf16x2(ts[i][2], ts[i][3])};
+            barrier_lds_sync();
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int b = 0; b < MB; ++b) {
-                    const u32x4 tf = u32x4{pack_bf16x2(lo[c][b][0], lo[c][b][1]), pack_bf16x2(lo[c][b][2], lo[c][b][3]),
-                                           pack_bf16x2(hi[c][b][0], hi[c][b][1]), pack_bf16x2(hi[c][b][2], hi[c][b][3])};
+                    // Lane's operand: ranks 8 (g % 2) .. +8 of fragment
+                    // 2 c + g / 2, row m = 16 b + l16 (rows past M hold zeros
+                    // and only reach outputs that are not stored).
+                    const u32x4 tf = *reinterpret_cast<const u32x4 *>(
+                        tb + ((2 * c + (g >> 1)) * 64 * MB + 4 * (16 * b + l16) + 2 * (g & 1)) * 8);
 #pragma unroll
                     for (int f = 0; f < WNF; ++f) acc[f][b] = mfma16(af[c][f], tf, acc[f][b]);
                 }
+            barrier_lds_sync();  // the next group's staging and bf16 T overwrite these
         }
     }
 
