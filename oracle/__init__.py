@@ -51,6 +51,11 @@ def _bind(lib):
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     lib.oracle_forward_rows.restype = ctypes.c_int
+    lib.oracle_quantize_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    lib.oracle_quantize_rows.restype = None
+    lib.oracle_forward_rows_act8.argtypes = lib.oracle_forward_rows.argtypes
+    lib.oracle_forward_rows_act8.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -83,14 +88,35 @@ def default_threads() -> int:
         return os.cpu_count() or 1
 
 
+def quantize_rows(x: torch.Tensor, lib=None):
+    """Activations in e4m3fn with one power-of-two scale per row.
+
+    x bf16 [M, in] -> (codes uint8 [M, in], e int32 [M]) with
+    x[m, j] ~ 2^e[m] * dec(codes[m, j]): e[m] is the smallest integer (at
+    least -126) with max_j |x[m, j]| <= 448 * 2^e[m], each code the nearest
+    e4m3fn value to x[m, j] / 2^e[m] with ties to even.  A row holding a NaN
+    or an infinity gets e = 0 and all codes 0x7F (NaN).
+    """
+    lib = lib or library()
+    xb = _bits16(x)
+    M, K = xb.shape
+    codes = np.empty((M, K), np.uint8)
+    exps = np.empty(M, np.int32)
+    lib.oracle_quantize_rows(_ptr(xb), M, K, _ptr(codes), _ptr(exps))
+    return codes, exps
+
+
 def forward(x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,
             Q: torch.Tensor, scale: float, bias: torch.Tensor | None,
-            rows=None, threads: int | None = None, want_T: bool = False, lib=None):
+            rows=None, threads: int | None = None, want_T: bool = False, lib=None,
+            act_fp8: bool = False):
     """float64 forward for all rows of x, or for the row indices in ``rows``.
 
     x bf16 [M, in]; A bf16 [out, r]; B bf16 [r, in]; Q uint8 e4m3fn codes
     [out, in]; scale a float32 value; bias bf16 [out] or None.  Returns y as
     float64 [len(rows), out], plus T [len(rows), r] when ``want_T``.
+    With ``act_fp8`` the residual product reads x quantised by
+    ``quantize_rows`` (the fp8-activation mode); T still reads the bf16 x.
     """
     lib = lib or library()
     M, K = x.shape
@@ -109,9 +135,10 @@ def forward(x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,
         nrows = ridx.size
     y = np.empty((nrows, N), np.float64)
     T = np.empty((nrows, max(r, 1)), np.float64) if want_T else None
-    rc = lib.oracle_forward_rows(_ptr(xb), _ptr(Ab), _ptr(Bb), _ptr(Qb), ctypes.c_float(scale),
-                                 _ptr(bb), M, K, N, r, _ptr(ridx), nrows, _ptr(y), _ptr(T),
-                                 int(threads or default_threads()))
+    fn = lib.oracle_forward_rows_act8 if act_fp8 else lib.oracle_forward_rows
+    rc = fn(_ptr(xb), _ptr(Ab), _ptr(Bb), _ptr(Qb), ctypes.c_float(scale),
+            _ptr(bb), M, K, N, r, _ptr(ridx), nrows, _ptr(y), _ptr(T),
+            int(threads or default_threads()))
     if rc != 0:
         raise ValueError("oracle_forward_rows rejected its arguments")
     if want_T:

@@ -160,6 +160,179 @@ int oracle_forward_rows(const uint16_t *x, const uint16_t *A, const uint16_t *B,
     return bad ? -1 : 0;
 }
 
+/*
+ * Activations in e4m3fn (the optional fp8-activation mode).  Each row of x
+ * gets a power-of-two scale 2^e, e the smallest integer with
+ * max_j |x[m,j]| <= 448 * 2^e (and e >= -126; e = -126 for an all-zero row),
+ * and every element becomes the e4m3fn code nearest to x[m,j] / 2^e, ties to
+ * the even code.  x[m,j] / 2^e is exact (a power-of-two scaling of a bf16
+ * value), so the only rounding is the one to e4m3fn.  A row holding a NaN or
+ * an infinity gets e = 0 and every code 0x7F (NaN).
+ */
+
+/* Nearest e4m3fn code to a finite v with |v| <= 448, ties to even. */
+static uint8_t e4m3fn_nearest(double v)
+{
+    int sign = v < 0 || (v == 0 && signbit(v));
+    double a = fabs(v), q;
+    int code, ex;
+    if (a < ldexp(1.0, -6)) {
+        /* zero and subnormals: multiples of 2^-9 (a result of 8 is 2^-6) */
+        q = a * 512.0;
+        double fl = floor(q);
+        double fr = q - fl;
+        int k = (int)fl;
+        if (fr > 0.5 || (fr == 0.5 && (k & 1)))
+            k += 1;
+        code = k; /* k == 8 is the code of 2^-6 */
+    } else {
+        /* normal: a = (1 + f/8) 2^ex with ex in [-6, 8] */
+        double mant = frexp(a, &ex); /* a = mant 2^ex, mant in [0.5, 1) */
+        ex -= 1;
+        mant *= 2.0;                 /* [1, 2) */
+        q = (mant - 1.0) * 8.0;      /* [0, 8) */
+        double fl = floor(q);
+        double fr = q - fl;
+        int f = (int)fl;
+#if ORACLE_PLANT == 8
+        if (fr >= 0.5) /* planted: ties away from zero */
+#else
+        if (fr > 0.5 || (fr == 0.5 && (f & 1)))
+#endif
+            f += 1;
+        if (f == 8) {
+            f = 0;
+            ex += 1;
+        }
+        code = ((ex + 7) << 3) | f;
+    }
+    return (uint8_t)(code | (sign << 7));
+}
+
+/* Scale exponent of a row (see above); returns 0 and sets *nonfinite for a
+ * row holding a NaN or an infinity. */
+static int row_scale_exp(const uint16_t *xr, int64_t in, int *nonfinite)
+{
+    double amax = 0.0;
+    int ex, e;
+    *nonfinite = 0;
+    for (int64_t j = 0; j < in; ++j) {
+        double v = oracle_bf16_to_f64(xr[j]);
+        if (!isfinite(v)) {
+            *nonfinite = 1;
+            return 0;
+        }
+        if (fabs(v) > amax)
+            amax = fabs(v);
+    }
+    if (amax == 0.0)
+        return -126;
+    /* amax = mant 2^ex, mant in [0.5, 1); 448 2^e = 0.875 2^(e + 9) */
+    double mant = frexp(amax, &ex);
+#if ORACLE_PLANT == 9
+    e = ex - 9; /* planted: the scale may leave amax above 448 */
+#else
+    e = mant <= 0.875 ? ex - 9 : ex - 8;
+#endif
+    return e < -126 ? -126 : e;
+}
+
+/*
+ * x bf16 bits [M, in] -> codes [M, in] and exponents e[M] (scale 2^e).
+ */
+void oracle_quantize_rows(const uint16_t *x, int64_t M, int64_t in, uint8_t *codes, int32_t *exps)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        int nonfinite;
+        int e = row_scale_exp(x + m * in, in, &nonfinite);
+        exps[m] = e;
+        for (int64_t j = 0; j < in; ++j)
+            codes[m * in + j] = nonfinite ? 0x7F : e4m3fn_nearest(ldexp(oracle_bf16_to_f64(x[m * in + j]), -e));
+    }
+}
+
+/*
+ * Forward of the fp8-activation mode for a list of rows: as
+ * oracle_forward_rows, but the residual product reads x as
+ * 2^e[m] * dec(codes[m, j]) (the row's quantised activations); the low-rank
+ * projection T = x B^T still reads the bf16 x.
+ */
+int oracle_forward_rows_act8(const uint16_t *x, const uint16_t *A, const uint16_t *B,
+                             const uint8_t *Q, float scale, const uint16_t *bias,
+                             int64_t M, int64_t in, int64_t out, int64_t r,
+                             const int64_t *rows, int64_t nrows, double *y, double *T,
+                             int nthreads)
+{
+    double dec[256];
+    double s = (double)scale;
+    int bad = 0;
+    if (M < 0 || in < 0 || out < 0 || r < 0 || nrows < 0 || !y)
+        return -1;
+    if (nrows > 0 && (!x || (out > 0 && in > 0 && !Q) || (r > 0 && (!A || !B))))
+        return -1;
+    for (int i = 0; i < 256; ++i)
+        dec[i] = oracle_e4m3fn_to_f64((uint8_t)i);
+    if (nthreads < 1)
+        nthreads = 1;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t m = rows ? rows[i] : i;
+        double *xr, *xq, *tr;
+        uint8_t *cr;
+        int32_t e;
+        if (m < 0 || m >= M) {
+            bad = 1;
+            continue;
+        }
+        xr = (double *)malloc(sizeof(double) * (size_t)(in > 0 ? in : 1));
+        xq = (double *)malloc(sizeof(double) * (size_t)(in > 0 ? in : 1));
+        tr = (double *)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
+        cr = (uint8_t *)malloc((size_t)(in > 0 ? in : 1));
+        if (!xr || !xq || !tr || !cr) {
+            free(xr);
+            free(xq);
+            free(tr);
+            free(cr);
+            bad = 1;
+            continue;
+        }
+        oracle_quantize_rows(x + m * in, 1, in, cr, &e);
+        for (int64_t j = 0; j < in; ++j) {
+            xr[j] = oracle_bf16_to_f64(x[m * in + j]);
+            xq[j] = ldexp(dec[cr[j]], e);
+        }
+        for (int64_t k = 0; k < r; ++k) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < in; ++j)
+#if ORACLE_PLANT == 10
+                acc += xq[j] * oracle_bf16_to_f64(B[k * in + j]); /* planted: T from the quantised x */
+#else
+                acc += xr[j] * oracle_bf16_to_f64(B[k * in + j]);
+#endif
+            tr[k] = acc;
+            if (T)
+                T[i * r + k] = acc;
+        }
+        for (int64_t n = 0; n < out; ++n) {
+            double lr = 0.0, res = 0.0, v;
+            for (int64_t k = 0; k < r; ++k)
+                lr += tr[k] * oracle_bf16_to_f64(A[n * r + k]);
+            for (int64_t j = 0; j < in; ++j)
+                res += xq[j] * dec[Q[n * in + j]];
+            v = lr + s * res;
+            if (bias)
+                v += oracle_bf16_to_f64(bias[n]);
+            y[i * out + n] = v;
+        }
+        free(xr);
+        free(xq);
+        free(tr);
+        free(cr);
+    }
+    return bad ? -1 : 0;
+}
+
 /* Reports how many OpenMP threads a parallel region actually gets. */
 int oracle_max_threads(void)
 {
