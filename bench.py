@@ -39,10 +39,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth
 MALL_BYTES = 256 << 20      # Infinity Cache
 COPY_PROBE_BYTES = 256 << 20
-KERNEL_NAMES = {"main": "fused_kernel", "pad_a": "pad_rows_kernel", "skinny": "skinny_kernel"}
+KERNEL_NAMES = {"main": "fused_kernel", "pad_a": "pad_rows_kernel", "skinny": "skinny_kernel",
+                "quant": "quant_rows_kernel"}
+# compute-bound workloads also measured with e4m3fn activations in the summary
+ACT8_SUMMARY = ("llm", "dit_r32", "dit_r64", "dit_r512", "large")
 HEADLINE = "dit_r64"
 
 
@@ -66,6 +70,8 @@ def parse():
     p.add_argument("--path", default="auto", choices=["auto", "skinny", "tiled"])
     p.add_argument("--split-k", type=int, default=0, help="skinny path: K-slice hint (0: automatic)")
     p.add_argument("--t-splits", type=int, default=0, help="tiled path: K slices per T block (0: automatic)")
+    p.add_argument("--act-fp8", action="store_true",
+                   help="e4m3fn activations for the residual product (LITELINEAR_OPT_ACT_FP8)")
     return p.parse_args()
 
 
@@ -79,7 +85,21 @@ def kernel_flops_bytes(w, kernel: str):
     if kernel == "pad_a":
         r_pad = -(-w.rank // 64) * 64
         return 0, 2 * w.out_features * (w.rank + r_pad)
+    if kernel == "quant":  # x read, codes and row scales written
+        return 0, 3 * w.M * w.in_features + 4 * w.M
     return w.flops, w.bytes
+
+
+def mfma_peak(w, act8: bool) -> float:
+    """Dense matrix-core peak for the main kernel's mix of work (TFLOP/s):
+    with e4m3fn activations the residual product runs at the fp8 rate and
+    the two low-rank products at the bf16 rate, so the peak is the work over
+    the time each part needs at its own rate."""
+    if not act8:
+        return PEAK_BF16_TFLOPS
+    M, K, N, r = w.M, w.in_features, w.out_features, w.rank
+    f8, f16 = 2 * M * K * N, 2 * M * r * (K + N)
+    return (f8 + f16) / (f8 / PEAK_FP8_TFLOPS + f16 / PEAK_BF16_TFLOPS)
 
 
 def source_digest() -> str:
@@ -112,7 +132,7 @@ def traffic_record(kernel: str, workload: str):
 class Runner:
     """Rotating resident copies of one workload's inputs and a handle."""
 
-    def __init__(self, w, args, dev, copies=0):
+    def __init__(self, w, args, dev, copies=0, act8=None):
         import torch
 
         from rank_fp8_residual_amd import Handle, Option, Path
@@ -133,6 +153,8 @@ class Runner:
         self.h.set_option(Option.PATH, {"auto": Path.AUTO, "skinny": Path.SKINNY, "tiled": Path.TILED}[args.path])
         self.h.set_option(Option.SPLIT_K, args.split_k)
         self.h.set_option(Option.T_SPLITS, args.t_splits)
+        self.act8 = args.act_fp8 if act8 is None else act8
+        self.h.set_option(Option.ACT_FP8, int(self.act8))
         self.dev = dev
 
     def step(self, i):
@@ -181,7 +203,8 @@ class Runner:
             self.step(i)
         torch.cuda.synchronize()
         kt = {}
-        for name, kind in (("pad_a", Kernel.PAD_A), ("main", Kernel.MAIN), ("skinny", Kernel.SKINNY)):
+        for name, kind in (("pad_a", Kernel.PAD_A), ("main", Kernel.MAIN), ("skinny", Kernel.SKINNY),
+                           ("quant", Kernel.QUANT)):
             ms, n = self.h.kernel_time(kind, reset=True)
             if n:
                 kt[name] = ms / n
@@ -195,7 +218,7 @@ class Runner:
         torch.cuda.empty_cache()
 
 
-def roofline(w, kt, ms_step):
+def roofline(w, kt, ms_step, act8=False):
     """Roofline of the dominant kernel.  Its duration per launch is the timed
     region's time per step when the step launches that kernel alone (events
     bracketing back-to-back launches, as a profiler's trace sees them), else
@@ -203,13 +226,16 @@ def roofline(w, kt, ms_step):
     dom = max(kt, key=kt.get)
     fl, by = kernel_flops_bytes(w, dom)
     dur_s = (ms_step if len(kt) == 1 else kt[dom]) * 1e-3
-    if fl and fl / by > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        roof = {"bound": "mfma", "achieved": round(fl / dur_s / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+    peak = mfma_peak(w, act8 and dom == "main")
+    if fl and fl / by > peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(fl / dur_s / 1e12, 2), "peak": round(peak, 1),
                 "unit": "TFLOP/s"}
+        if act8 and dom == "main":
+            roof["peak_note"] = "e4m3fn residual product at 5.0 PFLOP/s, bf16 low-rank products at 2.5 PFLOP/s"
     else:
         roof = {"bound": "hbm", "achieved": round(by / dur_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    rec = traffic_record(KERNEL_NAMES[dom], w.name)
+    rec = traffic_record(KERNEL_NAMES[dom], w.name + ("+act_fp8" if act8 else ""))
     roof["traffic"] = rec["hbm_bytes"] if rec else None
     if rec:
         roof["traffic_detail"] = {k: rec[k] for k in ("fetch_bytes", "write_bytes", "scale", "profile") if k in rec}
@@ -248,7 +274,7 @@ def main():
     log(f"timed {args.steps} steps: {ms_step * 1e3:.2f} us/step, {tflops:.1f} TFLOP/s, {gbs:.0f} GB/s")
     spread = run.step_spread(min(args.steps, 200))
     kt = run.kernel_times(args.steps)
-    roof = roofline(w, kt, ms_step)
+    roof = roofline(w, kt, ms_step, run.act8)
     log("kernel us", roof["kernel_us"], "event pairs", roof["kernel_us_event_pairs"], "traffic", roof["traffic"])
 
     cpu = None
@@ -259,22 +285,27 @@ def main():
     summary = None
     if not args.no_summary:
         summary = {}
-        for name, wo in wl.WORKLOADS.items():
-            if name == w.name:
+        cases = [(name, False) for name in wl.WORKLOADS] + [(name, True) for name in ACT8_SUMMARY]
+        for name, act8 in cases:
+            if name == w.name and act8 == run.act8:
                 continue
-            r = Runner(wo, args, dev)
+            wo = wl.WORKLOADS[name]
+            r = Runner(wo, args, dev, act8=act8)
             steps = 20 if wo.flops > 1e12 else 100
             ms = r.timed(20 if wo.flops > 1e12 else 300, steps)
             k = r.kernel_times(steps)
-            ro = roofline(wo, k, ms)
-            summary[name] = {
+            ro = roofline(wo, k, ms, act8)
+            key = name + ("+act_fp8" if act8 else "")
+            summary[key] = {
                 "M": wo.M, "in": wo.in_features, "out": wo.out_features, "r": wo.rank,
+                "activations": "e4m3fn" if act8 else "bf16",
                 "us_per_step": round(ms * 1e3, 2),
                 "TFLOP/s": round(wo.flops / (ms * 1e-3) / 1e12, 2),
                 "GB/s": round(wo.bytes / (ms * 1e-3) / 1e9, 1),
-                "roofline": {k2: ro[k2] for k2 in ("bound", "achieved", "unit", "frac", "kernel", "traffic")},
+                "kernel_us": {k2: round(v * 1e3, 2) for k2, v in k.items()},
+                "roofline": {k2: ro[k2] for k2 in ("bound", "achieved", "peak", "unit", "frac", "kernel", "traffic")},
             }
-            log(name, summary[name])
+            log(key, summary[key])
             r.release()
 
     if args.copy_probe:
@@ -292,15 +323,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "e4m3fn x e4m3fn residual, bf16 low-rank" if run.act8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: M={w.M} in={w.in_features} out={w.out_features} r={w.rank}; "
-                        "x/A/B/bias bf16, Q e4m3fn with per-tensor scale, y bf16",
+                        "x/A/B/bias bf16, Q e4m3fn with per-tensor scale, y bf16"
+                        + ("; x quantised to e4m3fn per row for the residual product" if run.act8 else ""),
             "M": w.M, "in": w.in_features, "out": w.out_features, "r": w.rank,
             "rotating_copies": run.copies, "hbm_GBps": round(gbs, 1),
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-            "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "mfma_frac": round(tflops / mfma_peak(w, run.act8), 4),
             "flops_per_step": w.flops, "bytes_per_step": w.bytes,
             "step_us": spread,
         },

@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kNumKernels = 3;
+constexpr int kNumKernels = 4;
 // Largest M sent to the skinny kernel when the path is chosen automatically.
 constexpr int64_t kSkinnyAutoMaxM = 64;
 
@@ -70,7 +70,11 @@ struct litelinear_ctx {
     size_t partials_bytes = 0;
     unsigned *counters = nullptr;
     size_t n_counters = 0;
-    int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0, opt_t_splits = 0;
+    void *xq = nullptr;             // fp8-activation mode: e4m3fn codes of x
+    size_t xq_bytes = 0;
+    float *xs = nullptr;            // ... and the rows' scales
+    size_t xs_bytes = 0;
+    int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0, opt_t_splits = 0, opt_act_fp8 = 0;
     Prof prof[kNumKernels];
     std::vector<hipEvent_t> event_pool;
 };
@@ -198,6 +202,8 @@ litelinear_status_t litelinear_destroy(litelinear_handle_t h) {
         if (h->a_pad) (void)hipFree(h->a_pad);
         if (h->partials) (void)hipFree(h->partials);
         if (h->counters) (void)hipFree(h->counters);
+        if (h->xq) (void)hipFree(h->xq);
+        if (h->xs) (void)hipFree(h->xs);
         for (auto &p : h->prof)
             for (auto &e : p.pending) {
                 (void)hipEventDestroy(e.first);
@@ -231,6 +237,10 @@ litelinear_status_t litelinear_set_option(litelinear_handle_t h, int key, int64_
         case LITELINEAR_OPT_T_SPLITS:
             if (value < 0 || value > 64) return LITELINEAR_ERR_INVALID_ARG;
             h->opt_t_splits = value;
+            return LITELINEAR_OK;
+        case LITELINEAR_OPT_ACT_FP8:
+            if (value != 0 && value != 1) return LITELINEAR_ERR_INVALID_ARG;
+            h->opt_act_fp8 = value;
             return LITELINEAR_OK;
     }
     return LITELINEAR_ERR_INVALID_ARG;
@@ -272,9 +282,12 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
     if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
 
     const int64_t r_pad = r > 0 ? cdiv(r, 64) * 64 : 0;
+    // The fp8-activation mode runs on the tiled kernel only (with in == 0
+    // there is no residual product to run in fp8).
+    const bool act8 = h->opt_act_fp8 != 0 && in > 0;
     int64_t path = h->opt_path;
     ll::SkinnyPlan plan{};
-    const bool skinny_ok = in > 0 && ll::skinny_supports(M) &&
+    const bool skinny_ok = !act8 && in > 0 && ll::skinny_supports(M) &&
                            ll::skinny_shape_ok(M, in, out, r_pad, plan = ll::skinny_plan(M, in, out, r_pad, h->opt_split));
     if (path == 0) path = (M <= kSkinnyAutoMaxM && skinny_ok) ? 1 : 2;
     if (path == 1 && !skinny_ok) return LITELINEAR_ERR_UNSUPPORTED;
@@ -357,6 +370,17 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
     p.out_f32 = out_f32;
     const ll::TileCfg mc = ll::choose_main_tile(p);
     if (!ll::tiled_shape_ok(p, mc)) return LITELINEAR_ERR_UNSUPPORTED;
+    if (act8) {
+        st = grow(&h->xq, &h->xq_bytes, (size_t)M * in, false);
+        if (st != LITELINEAR_OK) return st;
+        st = grow((void **)&h->xs, &h->xs_bytes, (size_t)M * sizeof(float), false);
+        if (st != LITELINEAR_OK) return st;
+        st = timed_launch(h, LITELINEAR_KERNEL_QUANT, stream,
+                          [&] { return ll::launch_quant_rows(x, h->xq, h->xs, M, in, stream); });
+        if (st != LITELINEAR_OK) return st;
+        p.xq = h->xq;
+        p.xs = h->xs;
+    }
     if (r > 0) {
         st = grow(&h->t_ws, &h->t_ws_bytes, (size_t)M * r_pad * 2, false);
         if (st != LITELINEAR_OK) return st;
@@ -386,6 +410,24 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
                       [&] { return ll::launch_tiled(p, mc, a_eff, h->tile_sync, stream); });
     if (st == LITELINEAR_OK && r > 0) ++h->tiled_epoch;
     return st;
+}
+
+litelinear_status_t litelinear_quantize_rows(litelinear_handle_t h, const void *x, int64_t M, int64_t in,
+                                             void *codes, float *scales, hipStream_t stream) {
+    if (!h || M < 0 || in < 0 || M > ((int64_t)1 << 40) || in > ((int64_t)1 << 40)) return LITELINEAR_ERR_INVALID_ARG;
+    if ((double)M * (double)in > 4.0e18) return LITELINEAR_ERR_INVALID_ARG;
+    if (M == 0) return LITELINEAR_OK;
+    if (!scales || (in > 0 && (!x || !codes))) return LITELINEAR_ERR_INVALID_ARG;
+    if (in % 16 != 0) return LITELINEAR_ERR_UNSUPPORTED;
+    if ((in > 0 && (!aligned(x, 16) || !aligned(codes, 8))) || !aligned(scales, 4)) return LITELINEAR_ERR_UNSUPPORTED;
+    if (in * 2 >= ((int64_t)1 << 31) || M >= ((int64_t)1 << 31)) return LITELINEAR_ERR_UNSUPPORTED;
+    const uint64_t nx = (uint64_t)M * in * 2, nc = (uint64_t)M * in, ns = (uint64_t)M * 4;
+    if (overlaps(codes, nc, x, nx) || overlaps(scales, ns, x, nx) || overlaps(scales, ns, codes, nc))
+        return LITELINEAR_ERR_INVALID_ARG;
+    DeviceGuard guard(h->device);
+    if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
+    return timed_launch(h, LITELINEAR_KERNEL_QUANT, stream,
+                        [&] { return ll::launch_quant_rows(x, codes, scales, M, in, stream); });
 }
 
 }  // extern "C"

@@ -23,6 +23,20 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 16x16x128 e4m3fn matrix-core product, float32 accumulate: c += a * b^T with
+// both operands e4m3fn codes.  Lane l holds row (l % 16) of `a` and of `b`
+// and 32 of the 128 reduction indices, the same 32 for both operands (a0/b0
+// the first 16 bytes, a1/b1 the next 16); the result layout is mfma16's.
+// Every product of two e4m3fn values is exact in float32.  The instruction's
+// block scales are left at 2^0 (E8M0 code 127).
+__device__ __forceinline__ f32x4 mfma16_f8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x4 c) {
+    const i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    const i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 // Four e4m3fn codes (bytes of `w`, lowest first) -> four bf16 values (two
 // dwords, lowest first).  gfx950's conversion instruction reads the OCP
 // e4m3fn encoding; with a multiplier of exactly 1.0 it is exact, because

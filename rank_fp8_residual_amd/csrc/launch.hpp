@@ -19,7 +19,16 @@ struct TiledProblem {
     int t_splits;        // K slices per T block (tiled_t_splits())
     unsigned t_target;   // row-tile counter value that marks this launch's T done
     bool out_f32;
+    // fp8-activation mode (both set, or both null): e4m3fn codes of x [M, K]
+    // and the rows' scales 2^e [M] from launch_quant_rows; the residual
+    // product reads these, T still reads x.
+    const void *xq;
+    const float *xs;
 };
+
+// x bf16 [M, K] (K % 8 == 0) -> e4m3fn codes [M, K] and one power-of-two
+// scale per row [M] (see quant.hip).
+hipError_t launch_quant_rows(const void *x, void *codes, float *scales, int64_t M, int64_t K, hipStream_t s);
 
 // Tile configuration of one launch (work-group tile BM x BN).
 struct TileCfg {

@@ -36,6 +36,7 @@ class Option(enum.IntEnum):
     SPLIT_K = 3
     PROFILE = 4
     T_SPLITS = 5
+    ACT_FP8 = 6
 
 
 class Path(enum.IntEnum):
@@ -48,11 +49,12 @@ class Kernel(enum.IntEnum):
     PAD_A = 0
     MAIN = 1
     SKINNY = 2
+    QUANT = 3
 
 
 EXPORTS = ("litelinear_create", "litelinear_forward", "litelinear_destroy", "litelinear_check_args",
            "litelinear_set_option", "litelinear_kernel_time", "litelinear_status_string",
-           "litelinear_version")
+           "litelinear_version", "litelinear_quantize_rows")
 
 
 class LiteLinearError(RuntimeError):
@@ -88,6 +90,8 @@ def lib(path: str | None = None) -> ctypes.CDLL:
         L.litelinear_kernel_time.restype = ctypes.c_int
         L.litelinear_status_string.argtypes = [ctypes.c_int]
         L.litelinear_status_string.restype = ctypes.c_char_p
+        L.litelinear_quantize_rows.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+        L.litelinear_quantize_rows.restype = ctypes.c_int
         L.litelinear_version.argtypes = []
         L.litelinear_version.restype = ctypes.c_char_p
         if path is None:
@@ -187,6 +191,31 @@ class Handle:
                                       out_features, r, s)
         _check(st, "litelinear_forward")
         return out.view(*lead, out_features)
+
+    def quantize_rows(self, x: torch.Tensor, codes: torch.Tensor | None = None,
+                      scales: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+        """x bf16 [M, in] -> (e4m3fn codes uint8 [M, in], row scales float32 [M]),
+        x[m, j] ~ scales[m] * dec(codes[m, j]) (see litelinear_quantize_rows)."""
+        dev = self.device
+        _expect(x, "x", torch.bfloat16, dev, 2)
+        M, K = x.shape
+        if codes is None:
+            codes = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        else:
+            _expect(codes, "codes", torch.uint8, dev, 2)
+            if codes.shape != (M, K):
+                raise ValueError("codes must have x's shape")
+        if scales is None:
+            scales = torch.empty((M,), dtype=torch.float32, device=dev)
+        else:
+            _expect(scales, "scales", torch.float32, dev, 1)
+            if scales.shape[0] != M:
+                raise ValueError("scales must have one element per row")
+        s = (stream or torch.cuda.current_stream(dev)).cuda_stream
+        ptr = lambda t: None if t.numel() == 0 else t.data_ptr()
+        _check(lib().litelinear_quantize_rows(self._h, ptr(x), M, K, ptr(codes), ptr(scales), s),
+               "litelinear_quantize_rows")
+        return codes, scales
 
 
 def _expect(t, name, dtype, dev, ndim):

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     lib = ctypes.CDLL(bind.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -90,6 +90,7 @@ def test_null_handle_calls_fail_cleanly():
     assert L.litelinear_create(None, 0) == INV
     assert L.litelinear_forward(None, None, None, None, None, ctypes.c_float(1.0), None, None,
                                 1, 16, 16, 0, None) == INV
+    assert L.litelinear_quantize_rows(None, None, 1, 16, None, None, None) == INV
 
 
 def test_binding_refuses_missing_library(tmp_path):
