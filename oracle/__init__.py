@@ -56,6 +56,11 @@ def _bind(lib):
     lib.oracle_quantize_rows.restype = None
     lib.oracle_forward_rows_act8.argtypes = lib.oracle_forward_rows.argtypes
     lib.oracle_forward_rows_act8.restype = ctypes.c_int
+    lib.oracle_residual.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    lib.oracle_residual.restype = None
+    lib.oracle_quantize_tensor.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.oracle_quantize_tensor.restype = ctypes.c_float
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -104,6 +109,31 @@ def quantize_rows(x: torch.Tensor, lib=None):
     exps = np.empty(M, np.int32)
     lib.oracle_quantize_rows(_ptr(xb), M, K, _ptr(codes), _ptr(exps))
     return codes, exps
+
+
+def residual(W: torch.Tensor, A: torch.Tensor, B: torch.Tensor, lib=None) -> np.ndarray:
+    """R = W - A B in float64 (W bf16 [out, in], A bf16 [out, r], B bf16 [r, in])."""
+    lib = lib or library()
+    out, K = W.shape
+    r = A.shape[1]
+    assert A.shape == (out, r) and B.shape == (r, K)
+    Wb, Ab, Bb = _bits16(W), _bits16(A), _bits16(B)
+    R = np.empty((out, K), np.float64)
+    lib.oracle_residual(_ptr(Wb), _ptr(Ab), _ptr(Bb), out, K, r, _ptr(R))
+    return R
+
+
+def quantize_tensor(R, lib=None):
+    """Per-tensor e4m3fn codes of a float32 array: (codes uint8, scale float).
+
+    scale = amax / 448 in float32 (1 for an all-zero array); each code is the
+    e4m3fn value nearest to the float32 quotient R / scale clamped to +-448.
+    """
+    lib = lib or library()
+    Rf = np.ascontiguousarray(np.asarray(R, dtype=np.float32))
+    codes = np.empty(Rf.shape, np.uint8)
+    s = lib.oracle_quantize_tensor(_ptr(Rf), Rf.size, _ptr(codes))
+    return codes, float(np.float32(s))
 
 
 def forward(x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,

@@ -333,6 +333,59 @@ int oracle_forward_rows_act8(const uint16_t *x, const uint16_t *A, const uint16_
     return bad ? -1 : 0;
 }
 
+/*
+ * Decomposition side (the step upstream of the forward: LiteLinear README,
+ * *Usage*, "From a dense nn.Linear": LiteLinear.from_dense, SVD-based;
+ * *Features*: W ~ A.B + Q_fp8 with a per-tensor Q_scale_inv).
+ *
+ * Residual: R = W - A B in double, W bf16 [out, in], A bf16 [out, r],
+ * B bf16 [r, in].
+ */
+void oracle_residual(const uint16_t *W, const uint16_t *A, const uint16_t *B, int64_t out, int64_t in,
+                     int64_t r, double *R)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < out; ++n)
+        for (int64_t j = 0; j < in; ++j) {
+            double ab = 0.0;
+            for (int64_t k = 0; k < r; ++k)
+#if ORACLE_PLANT == 11
+                ab += oracle_bf16_to_f64(A[n * r + k]) * oracle_bf16_to_f64(B[j * r + k]); /* planted: B read transposed */
+#else
+                ab += oracle_bf16_to_f64(A[n * r + k]) * oracle_bf16_to_f64(B[k * in + j]);
+#endif
+            R[n * in + j] = oracle_bf16_to_f64(W[n * in + j]) - ab;
+        }
+}
+
+/*
+ * Per-tensor e4m3fn quantiser of a float32 residual: s = amax / 448 in
+ * float32 (1 when amax is 0), and each code the e4m3fn value nearest to
+ * the float32 quotient R / s clamped to +-448 (ties to even).  R must be
+ * finite.  Returns s; the dequantised residual is s * dec(code).
+ */
+float oracle_quantize_tensor(const float *R, int64_t n, uint8_t *codes)
+{
+    float amax = 0.0f, s;
+    for (int64_t i = 0; i < n; ++i)
+        if (fabsf(R[i]) > amax)
+            amax = fabsf(R[i]);
+#if ORACLE_PLANT == 12
+    s = amax > 0.0f ? amax / 240.0f : 1.0f; /* planted: the fnuz maximum */
+#else
+    s = amax > 0.0f ? amax / 448.0f : 1.0f;
+#endif
+    for (int64_t i = 0; i < n; ++i) {
+        float q = R[i] / s;
+        if (q > 448.0f)
+            q = 448.0f;
+        if (q < -448.0f)
+            q = -448.0f;
+        codes[i] = e4m3fn_nearest((double)q);
+    }
+    return s;
+}
+
 /* Reports how many OpenMP threads a parallel region actually gets. */
 int oracle_max_threads(void)
 {
