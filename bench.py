@@ -47,6 +47,8 @@ KERNEL_NAMES = {"main": "fused_kernel", "pad_a": "pad_rows_kernel", "skinny": "s
                 "quant": "quant_rows_kernel"}
 # compute-bound workloads also measured with e4m3fn activations in the summary
 ACT8_SUMMARY = ("llm", "dit_r32", "dit_r64", "dit_r512", "large")
+# weights whose decomposition step (residual + e4m3fn quantisation) is timed
+CONVERT_SUMMARY = ("dit_r64", "large")
 HEADLINE = "dit_r64"
 
 
@@ -308,6 +310,11 @@ def main():
             log(key, summary[key])
             r.release()
 
+        for name in CONVERT_SUMMARY:
+            key = "convert+" + name
+            summary[key] = convert_timing(wl.WORKLOADS[name], dev)
+            log(key, summary[key])
+
     if args.copy_probe:
         copy_probe(dev)
 
@@ -341,6 +348,55 @@ def main():
         "workloads": summary,
     }
     print(json.dumps(line), flush=True)
+
+
+def convert_timing(w, dev, steps=20):
+    """litelinear_residual_quantize on the workload's weight shapes (W [out, in]
+    bf16, rank r): e4m3fn codes and scale of W - A B.  Both passes read W;
+    algorithmic bytes count W, A, B once and the codes once."""
+    import torch
+
+    from rank_fp8_residual_amd import Handle
+
+    out_f, in_f, r = w.out_features, w.in_features, w.rank
+    nbytes = 2 * out_f * in_f + 2 * r * (out_f + in_f) + out_f * in_f
+    copies = max(2, min(16, math.ceil(4 * MALL_BYTES / nbytes)))
+    g = torch.Generator(device="cpu").manual_seed(7)
+    sets = []
+    for _ in range(copies):
+        W = (torch.randn(out_f, in_f, generator=g) * 0.05).to(torch.bfloat16).to(dev)
+        A = (torch.randn(out_f, r, generator=g) * 0.01).to(torch.bfloat16).to(dev)
+        B = torch.randn(r, in_f, generator=g).to(torch.bfloat16).to(dev)
+        codes = torch.empty((out_f, in_f), dtype=torch.uint8, device=dev)
+        sets.append((W, A, B, codes))
+    scale = torch.empty((1,), dtype=torch.float32, device=dev)
+    h = Handle(dev.index)
+    from rank_fp8_residual_amd import litelinear as L
+
+    def step(i):
+        W, A, B, codes = sets[i % copies]
+        st = L.lib().litelinear_residual_quantize(h._h, W.data_ptr(), A.data_ptr(), B.data_ptr(), out_f, in_f, r,
+                                                  codes.data_ptr(), scale.data_ptr(),
+                                                  torch.cuda.current_stream(dev).cuda_stream)
+        if st:
+            raise RuntimeError(f"litelinear_residual_quantize: status {st}")
+
+    for i in range(5):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2 * 2 * out_f * in_f * r  # A B in each of the two passes
+    del sets
+    torch.cuda.empty_cache()
+    return {"out": out_f, "in": in_f, "r": r, "us_per_call": round(ms * 1e3, 2),
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2), "algorithmic_bytes": nbytes}
 
 
 def copy_probe(dev, reps=5):

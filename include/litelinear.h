@@ -87,7 +87,9 @@ typedef enum {
                                      only when r % 8 != 0 or A is not 16-byte aligned) */
     LITELINEAR_KERNEL_MAIN = 1,   /* tiled path: T = x B^T, residual, rank-r product and bias */
     LITELINEAR_KERNEL_SKINNY = 2, /* skinny path: the same in one launch of its own kernel */
-    LITELINEAR_KERNEL_QUANT = 3   /* activations to e4m3fn (LITELINEAR_OPT_ACT_FP8, litelinear_quantize_rows) */
+    LITELINEAR_KERNEL_QUANT = 3,  /* activations to e4m3fn (LITELINEAR_OPT_ACT_FP8, litelinear_quantize_rows) */
+    LITELINEAR_KERNEL_CONVERT = 4 /* decomposition side: litelinear_quantize_tensor, litelinear_residual_quantize
+                                     (both passes of one call count as one launch) */
 } litelinear_kernel_t;
 
 /*
@@ -149,6 +151,38 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h,
  */
 litelinear_status_t litelinear_quantize_rows(litelinear_handle_t h, const void *x, int64_t M, int64_t in,
                                              void *codes, float *scales, hipStream_t stream);
+
+/*
+ * Decomposition side (LiteLinear README, *Usage*: LiteLinear.from_dense
+ * builds the pair by an SVD of the dense weight; *Features*:
+ * W ~ A B + Q_fp8 with Q_fp8 in e4m3fn and a per-tensor Q_scale_inv).
+ *
+ * litelinear_quantize_tensor: per-tensor e4m3fn codes of a float32 array.
+ *   R          float32 [n]  16-byte aligned, finite; n % 4 == 0.
+ *   codes      uint8   [n]  4-byte aligned.
+ *   scale_out  float32 device pointer: s = max|R| / 448 (1 when R is all
+ *              zero), a correctly rounded float32 division.
+ *   codes[i] is the e4m3fn value nearest to clamp(R[i] / s, -448, 448), the
+ *   quotient a correctly rounded float32 division, ties to the even code;
+ *   R ~ s * dec(codes) (the forward's Q and scale).
+ *
+ * litelinear_residual_quantize: the same for R = W - A B, computed on the
+ * device in float32 (bf16 products, float32 sums) and never stored.
+ *   W      bf16 [out, in] 16-byte aligned, in % 16 == 0.
+ *   A      bf16 [out, r]  16-byte aligned, r % 8 == 0 (may be NULL iff r == 0).
+ *   B      bf16 [r, in]   16-byte aligned (may be NULL iff r == 0).
+ *   codes  uint8 [out, in] 4-byte aligned; scale_out as above.
+ *
+ * Both read their input twice (max |R|, then the codes), use one word of
+ * the handle's workspace, and are queued on `stream`.  Outputs must not
+ * overlap the inputs.  Errors: INVALID_ARG, UNSUPPORTED (alignment, the
+ * multiples above, tensors of 2^31 bytes or more), HIP, OOM.
+ */
+litelinear_status_t litelinear_quantize_tensor(litelinear_handle_t h, const float *R, int64_t n, void *codes,
+                                               float *scale_out, hipStream_t stream);
+litelinear_status_t litelinear_residual_quantize(litelinear_handle_t h, const void *W, const void *A, const void *B,
+                                                 int64_t out, int64_t in, int64_t r, void *codes, float *scale_out,
+                                                 hipStream_t stream);
 
 /* Frees the handle and its workspace (synchronising the device first).
  * NULL is accepted. */

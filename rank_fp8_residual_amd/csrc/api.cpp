@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kNumKernels = 4;
+constexpr int kNumKernels = 5;
 // Largest M sent to the skinny kernel when the path is chosen automatically.
 constexpr int64_t kSkinnyAutoMaxM = 64;
 
@@ -74,6 +74,8 @@ struct litelinear_ctx {
     size_t xq_bytes = 0;
     float *xs = nullptr;            // ... and the rows' scales
     size_t xs_bytes = 0;
+    unsigned *amax = nullptr;       // decomposition side: max |R| as float bits
+    size_t amax_bytes = 0;
     int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0, opt_t_splits = 0, opt_act_fp8 = 0;
     Prof prof[kNumKernels];
     std::vector<hipEvent_t> event_pool;
@@ -204,6 +206,7 @@ litelinear_status_t litelinear_destroy(litelinear_handle_t h) {
         if (h->counters) (void)hipFree(h->counters);
         if (h->xq) (void)hipFree(h->xq);
         if (h->xs) (void)hipFree(h->xs);
+        if (h->amax) (void)hipFree(h->amax);
         for (auto &p : h->prof)
             for (auto &e : p.pending) {
                 (void)hipEventDestroy(e.first);
@@ -428,6 +431,67 @@ litelinear_status_t litelinear_quantize_rows(litelinear_handle_t h, const void *
     if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
     return timed_launch(h, LITELINEAR_KERNEL_QUANT, stream,
                         [&] { return ll::launch_quant_rows(x, codes, scales, M, in, stream); });
+}
+
+litelinear_status_t litelinear_quantize_tensor(litelinear_handle_t h, const float *R, int64_t n, void *codes,
+                                               float *scale_out, hipStream_t stream) {
+    if (!h || n < 0 || n > ((int64_t)1 << 40)) return LITELINEAR_ERR_INVALID_ARG;
+    if (!scale_out || (n > 0 && (!R || !codes))) return LITELINEAR_ERR_INVALID_ARG;
+    if (n % 4 != 0) return LITELINEAR_ERR_UNSUPPORTED;
+    if ((n > 0 && (!aligned(R, 16) || !aligned(codes, 4))) || !aligned(scale_out, 4)) return LITELINEAR_ERR_UNSUPPORTED;
+    if (n * 4 >= ((int64_t)1 << 31)) return LITELINEAR_ERR_UNSUPPORTED;
+    if (overlaps(codes, (uint64_t)n, R, (uint64_t)n * 4) || overlaps(scale_out, 4, R, (uint64_t)n * 4) ||
+        overlaps(scale_out, 4, codes, (uint64_t)n))
+        return LITELINEAR_ERR_INVALID_ARG;
+    DeviceGuard guard(h->device);
+    if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
+    litelinear_status_t st = grow((void **)&h->amax, &h->amax_bytes, 256, false);
+    if (st != LITELINEAR_OK) return st;
+    if (n == 0) {
+        const float one = 1.0f;  // scale of an empty (all-zero) tensor
+        return hipMemcpyAsync(scale_out, &one, 4, hipMemcpyHostToDevice, stream) == hipSuccess &&
+                       hipStreamSynchronize(stream) == hipSuccess
+                   ? LITELINEAR_OK
+                   : LITELINEAR_ERR_HIP;
+    }
+    return timed_launch(h, LITELINEAR_KERNEL_CONVERT, stream,
+                        [&] { return ll::launch_quant_tensor(R, n, codes, h->amax, scale_out, stream); });
+}
+
+litelinear_status_t litelinear_residual_quantize(litelinear_handle_t h, const void *W, const void *A, const void *B,
+                                                 int64_t out, int64_t in, int64_t r, void *codes, float *scale_out,
+                                                 hipStream_t stream) {
+    const int64_t lim = (int64_t)1 << 40;
+    if (!h || out < 0 || in < 0 || r < 0 || out > lim || in > lim || r > lim) return LITELINEAR_ERR_INVALID_ARG;
+    if ((double)out * (double)in > 4.0e18 || (double)r * (double)(in + out) > 4.0e18) return LITELINEAR_ERR_INVALID_ARG;
+    if (!scale_out) return LITELINEAR_ERR_INVALID_ARG;
+    if (out > 0 && in > 0 && (!W || !codes || (r > 0 && (!A || !B)))) return LITELINEAR_ERR_INVALID_ARG;
+    if (in % 16 != 0 || r % 8 != 0) return LITELINEAR_ERR_UNSUPPORTED;
+    if (!aligned(scale_out, 4) || (out > 0 && in > 0 && (!aligned(W, 16) || !aligned(codes, 4))) ||
+        (r > 0 && out > 0 && in > 0 && (!aligned(A, 16) || !aligned(B, 16))))
+        return LITELINEAR_ERR_UNSUPPORTED;
+    const int64_t l31 = (int64_t)1 << 31;
+    if (out * in * 2 >= l31 || out * r * 2 >= l31 || r * in * 2 >= l31) return LITELINEAR_ERR_UNSUPPORTED;
+    const uint64_t nc = (uint64_t)out * in;
+    if (overlaps(codes, nc, W, nc * 2) || (r > 0 && (overlaps(codes, nc, A, (uint64_t)out * r * 2) ||
+                                                     overlaps(codes, nc, B, (uint64_t)r * in * 2))) ||
+        overlaps(scale_out, 4, codes, nc) || overlaps(scale_out, 4, W, nc * 2))
+        return LITELINEAR_ERR_INVALID_ARG;
+    DeviceGuard guard(h->device);
+    if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
+    litelinear_status_t st = grow((void **)&h->amax, &h->amax_bytes, 256, false);
+    if (st != LITELINEAR_OK) return st;
+    if (out == 0 || in == 0) {
+        const float one = 1.0f;
+        return hipMemcpyAsync(scale_out, &one, 4, hipMemcpyHostToDevice, stream) == hipSuccess &&
+                       hipStreamSynchronize(stream) == hipSuccess
+                   ? LITELINEAR_OK
+                   : LITELINEAR_ERR_HIP;
+    }
+    return timed_launch(h, LITELINEAR_KERNEL_CONVERT, stream, [&] {
+        return ll::launch_residual_quant(W, r > 0 ? A : nullptr, r > 0 ? B : nullptr, out, in, r, codes, h->amax,
+                                         scale_out, stream);
+    });
 }
 
 }  // extern "C"

@@ -30,6 +30,16 @@ struct TiledProblem {
 // scale per row [M] (see quant.hip).
 hipError_t launch_quant_rows(const void *x, void *codes, float *scales, int64_t M, int64_t K, hipStream_t s);
 
+// Decomposition side (convert.hip).  amax_bits: one device word of
+// workspace, cleared on the stream by each call.
+// float32 R [n] (n % 4 == 0) -> codes [n], *scale_out = max|R| / 448.
+hipError_t launch_quant_tensor(const float *R, int64_t n, void *codes, unsigned *amax_bits, float *scale_out,
+                               hipStream_t s);
+// R = W - A B (W bf16 [N, K], A bf16 [N, r], B bf16 [r, K]; K % 16 == 0,
+// r % 8 == 0) -> codes [N, K], *scale_out = max|R| / 448.
+hipError_t launch_residual_quant(const void *W, const void *A, const void *B, int64_t N, int64_t K, int64_t r,
+                                 void *codes, unsigned *amax_bits, float *scale_out, hipStream_t s);
+
 // Tile configuration of one launch (work-group tile BM x BN).
 struct TileCfg {
     int bm, bn;

@@ -50,11 +50,13 @@ class Kernel(enum.IntEnum):
     MAIN = 1
     SKINNY = 2
     QUANT = 3
+    CONVERT = 4
 
 
 EXPORTS = ("litelinear_create", "litelinear_forward", "litelinear_destroy", "litelinear_check_args",
            "litelinear_set_option", "litelinear_kernel_time", "litelinear_status_string",
-           "litelinear_version", "litelinear_quantize_rows")
+           "litelinear_version", "litelinear_quantize_rows", "litelinear_quantize_tensor",
+           "litelinear_residual_quantize")
 
 
 class LiteLinearError(RuntimeError):
@@ -92,6 +94,10 @@ def lib(path: str | None = None) -> ctypes.CDLL:
         L.litelinear_status_string.restype = ctypes.c_char_p
         L.litelinear_quantize_rows.argtypes = [vp, vp, i64, i64, vp, vp, vp]
         L.litelinear_quantize_rows.restype = ctypes.c_int
+        L.litelinear_quantize_tensor.argtypes = [vp, vp, i64, vp, vp, vp]
+        L.litelinear_quantize_tensor.restype = ctypes.c_int
+        L.litelinear_residual_quantize.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
+        L.litelinear_residual_quantize.restype = ctypes.c_int
         L.litelinear_version.argtypes = []
         L.litelinear_version.restype = ctypes.c_char_p
         if path is None:
@@ -216,6 +222,45 @@ class Handle:
         _check(lib().litelinear_quantize_rows(self._h, ptr(x), M, K, ptr(codes), ptr(scales), s),
                "litelinear_quantize_rows")
         return codes, scales
+
+    def quantize_tensor(self, R: torch.Tensor, stream: torch.cuda.Stream | None = None):
+        """float32 R -> (e4m3fn codes uint8 of R's shape, scale float32 [1] on
+        the device), R ~ scale * dec(codes) (see litelinear_quantize_tensor)."""
+        dev = self.device
+        _expect(R, "R", torch.float32, dev, None)
+        codes = torch.empty(R.shape, dtype=torch.uint8, device=dev)
+        scale = torch.empty((1,), dtype=torch.float32, device=dev)
+        s = (stream or torch.cuda.current_stream(dev)).cuda_stream
+        ptr = lambda t: None if t.numel() == 0 else t.data_ptr()
+        _check(lib().litelinear_quantize_tensor(self._h, ptr(R), R.numel(), ptr(codes), scale.data_ptr(), s),
+               "litelinear_quantize_tensor")
+        return codes, scale
+
+    def residual_quantize(self, W: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,
+                          stream: torch.cuda.Stream | None = None):
+        """e4m3fn codes and per-tensor scale of R = W - A B (the forward's Q and
+        scale for the pair A, B; see litelinear_residual_quantize)."""
+        dev = self.device
+        _expect(W, "W", torch.bfloat16, dev, 2)
+        out_features, in_features = W.shape
+        if A is None or B is None:
+            if (A is None) != (B is None):
+                raise ValueError("A and B must both be given or both be None")
+            r = 0
+        else:
+            _expect(A, "A", torch.bfloat16, dev, 2)
+            _expect(B, "B", torch.bfloat16, dev, 2)
+            r = A.shape[1]
+            if A.shape[0] != out_features or B.shape != (r, in_features):
+                raise ValueError("A / B do not match W")
+        codes = torch.empty((out_features, in_features), dtype=torch.uint8, device=dev)
+        scale = torch.empty((1,), dtype=torch.float32, device=dev)
+        s = (stream or torch.cuda.current_stream(dev)).cuda_stream
+        ptr = lambda t: None if t is None or t.numel() == 0 else t.data_ptr()
+        _check(lib().litelinear_residual_quantize(self._h, ptr(W), ptr(A) if r else None, ptr(B) if r else None,
+                                                  out_features, in_features, r, ptr(codes), scale.data_ptr(), s),
+               "litelinear_residual_quantize")
+        return codes, scale
 
 
 def _expect(t, name, dtype, dev, ndim):
