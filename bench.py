@@ -314,6 +314,8 @@ def main():
             key = "convert+" + name
             summary[key] = convert_timing(wl.WORKLOADS[name], dev)
             log(key, summary[key])
+        summary["pair+dit_r64"] = pair_timing(wl.WORKLOADS["dit_r64"], args, dev)
+        log("pair+dit_r64", summary["pair+dit_r64"])
 
     if args.copy_probe:
         copy_probe(dev)
@@ -348,6 +350,44 @@ def main():
         "workloads": summary,
     }
     print(json.dumps(line), flush=True)
+
+
+def pair_timing(w, args, dev, steps=100):
+    """litelinear_forward_pair on two outputs of the workload's shape sharing
+    x and B (a gate/up pair), against the same two outputs as two forwards."""
+    import torch
+
+    from rank_fp8_residual_amd import Handle
+    from rank_fp8_residual_amd import workloads as wl
+
+    d1 = wl.make_inputs(w, seed=args.seed)
+    d2 = wl.make_inputs(w, seed=args.seed + 1)
+    t = lambda v: v.to(dev) if isinstance(v, torch.Tensor) else v
+    g1 = {k: t(v) for k, v in d1.items()}
+    g2 = {k: t(v) for k, v in d2.items()}
+    g2["x"], g2["B"] = g1["x"], g1["B"]
+    y1 = torch.empty((w.M, w.out_features), dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty_like(y1)
+    h = Handle(dev.index)
+    pair = lambda: h.forward_pair(g1["x"], g1["B"], (g1["A"], g1["Q"], g1["scale"], g1["bias"]),
+                                  (g2["A"], g2["Q"], g2["scale"], g2["bias"]), out=(y1, y2))
+    two = lambda: (h.forward(g1["x"], g1["A"], g1["B"], g1["Q"], g1["scale"], g1["bias"], out=y1),
+                   h.forward(g2["x"], g2["A"], g2["B"], g2["Q"], g2["scale"], g2["bias"], out=y2))
+    res = {}
+    for name, fn in (("pair", pair), ("two_forwards", two)):
+        for _ in range(50):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name + "_us"] = round(e0.elapsed_time(e1) / steps * 1e3, 2)
+    res["TFLOP/s_pair"] = round(2 * w.flops / (res["pair_us"] * 1e-6) / 1e12, 2)
+    res["note"] = "two outputs of this shape sharing x and B; T computed once by the pair"
+    return res
 
 
 def convert_timing(w, dev, steps=20):

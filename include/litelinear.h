@@ -184,6 +184,23 @@ litelinear_status_t litelinear_residual_quantize(litelinear_handle_t h, const vo
                                                  int64_t out, int64_t in, int64_t r, void *codes, float *scale_out,
                                                  hipStream_t stream);
 
+/*
+ * Two outputs that share x and B, and so T = x B^T (a gate/up pair; the
+ * modegpt_compressor page's shared factors are the analogue on the other
+ * side of the product):
+ *     y1 = T A1^T + scale1 * (x dec(Q1)^T) + bias1      y1 [M, out1]
+ *     y2 = T A2^T + scale2 * (x dec(Q2)^T) + bias2      y2 [M, out2]
+ * Each output's tensors follow litelinear_forward's rules; the outputs must
+ * not overlap each other or any input.  Large M runs one tiled launch that
+ * computes T once for both; with M in the skinny regime (or out1 or out2 0)
+ * it runs one forward per output.  Options as for litelinear_forward.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP, OOM.
+ */
+litelinear_status_t litelinear_forward_pair(litelinear_handle_t h, const void *x, const void *B, const void *A1,
+                                            const void *Q1, float scale1, const void *bias1, void *y1, int64_t out1,
+                                            const void *A2, const void *Q2, float scale2, const void *bias2, void *y2,
+                                            int64_t out2, int64_t M, int64_t in, int64_t r, hipStream_t stream);
+
 /* Frees the handle and its workspace (synchronising the device first).
  * NULL is accepted. */
 litelinear_status_t litelinear_destroy(litelinear_handle_t h);

@@ -66,6 +66,10 @@ struct litelinear_ctx {
     uint64_t tiled_key = 0, skinny_key = 0;  // layout the counters were last used with
     void *a_pad = nullptr;          // tiled path: zero-padded copy of A
     size_t a_pad_bytes = 0;
+    void *a_pad2 = nullptr;         // ... and of a pair's second A
+    size_t a_pad2_bytes = 0;
+    void *t_ws2 = nullptr;          // a pair's second T' workspace
+    size_t t_ws2_bytes = 0;
     float *partials = nullptr;
     size_t partials_bytes = 0;
     unsigned *counters = nullptr;
@@ -202,6 +206,8 @@ litelinear_status_t litelinear_destroy(litelinear_handle_t h) {
         if (h->tile_sync) (void)hipFree(h->tile_sync);
         if (h->t_part) (void)hipFree(h->t_part);
         if (h->a_pad) (void)hipFree(h->a_pad);
+        if (h->a_pad2) (void)hipFree(h->a_pad2);
+        if (h->t_ws2) (void)hipFree(h->t_ws2);
         if (h->partials) (void)hipFree(h->partials);
         if (h->counters) (void)hipFree(h->counters);
         if (h->xq) (void)hipFree(h->xq);
@@ -273,16 +279,28 @@ litelinear_status_t litelinear_kernel_time(litelinear_handle_t h, int kernel, do
     return st;
 }
 
-litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, const void *A, const void *B,
-                                       const void *Q, float scale, const void *bias, void *y, int64_t M,
-                                       int64_t in, int64_t out, int64_t r, hipStream_t stream) {
-    if (!h) return LITELINEAR_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// One output of a forward: y [M, out] = (x B^T) A^T + scale x dec(Q)^T + bias.
+struct OutSet {
+    const void *A, *Q, *bias;
+    float scale;
+    void *y;
+    int64_t out;
+};
+
+// The forward for one output, or for two sharing x and B (s2 != nullptr:
+// the tiled kernel, T computed once).  Arguments are already checked.
+litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, const void *B, const OutSet &s1, const OutSet *s2,
+                                 int64_t M, int64_t in, int64_t r, hipStream_t stream) {
+    const void *A = s1.A, *Q = s1.Q, *bias = s1.bias;
+    void *y = s1.y;
+    const float scale = s1.scale;
+    const int64_t out = s1.out;
     const bool out_f32 = h->opt_out_f32 != 0;
-    litelinear_status_t st = litelinear_check_args(x, A, B, Q, bias, y, M, in, out, r, out_f32 ? 4 : 2);
-    if (st != LITELINEAR_OK) return st;
-    if (M == 0 || out == 0) return LITELINEAR_OK;
-    DeviceGuard guard(h->device);
-    if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
+    litelinear_status_t st = LITELINEAR_OK;
 
     const int64_t r_pad = r > 0 ? cdiv(r, 64) * 64 : 0;
     // The fp8-activation mode runs on the tiled kernel only (with in == 0
@@ -292,6 +310,7 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
     ll::SkinnyPlan plan{};
     const bool skinny_ok = !act8 && in > 0 && ll::skinny_supports(M) &&
                            ll::skinny_shape_ok(M, in, out, r_pad, plan = ll::skinny_plan(M, in, out, r_pad, h->opt_split));
+    if (s2) path = 2;
     if (path == 0) path = (M <= kSkinnyAutoMaxM && skinny_ok) ? 1 : 2;
     if (path == 1 && !skinny_ok) return LITELINEAR_ERR_UNSUPPORTED;
 
@@ -305,6 +324,15 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
                           [&] { return ll::launch_pad_a(A, h->a_pad, out, r, r_pad, stream); });
         if (st != LITELINEAR_OK) return st;
         a_eff = h->a_pad;
+    }
+    const void *a_eff2 = s2 ? s2->A : nullptr;
+    if (s2 && ll::a_needs_padding(r, s2->A)) {
+        st = grow(&h->a_pad2, &h->a_pad2_bytes, (size_t)s2->out * r_pad * 2, false);
+        if (st != LITELINEAR_OK) return st;
+        st = timed_launch(h, LITELINEAR_KERNEL_PAD_A, stream,
+                          [&] { return ll::launch_pad_a(s2->A, h->a_pad2, s2->out, r, r_pad, stream); });
+        if (st != LITELINEAR_OK) return st;
+        a_eff2 = h->a_pad2;
     }
 
     if (path == 1) {
@@ -371,6 +399,14 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
     p.r = r;
     p.r_pad = r_pad;
     p.out_f32 = out_f32;
+    if (s2) {
+        p.Q2 = s2->Q;
+        p.A2 = s2->A;
+        p.bias2 = s2->bias;
+        p.y2 = s2->y;
+        p.scale2 = s2->scale;
+        p.N2 = s2->out;
+    }
     const ll::TileCfg mc = ll::choose_main_tile(p);
     if (!ll::tiled_shape_ok(p, mc)) return LITELINEAR_ERR_UNSUPPORTED;
     if (act8) {
@@ -388,6 +424,11 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
         st = grow(&h->t_ws, &h->t_ws_bytes, (size_t)M * r_pad * 2, false);
         if (st != LITELINEAR_OK) return st;
         p.t_ws = h->t_ws;
+        if (s2) {
+            st = grow(&h->t_ws2, &h->t_ws2_bytes, (size_t)M * r_pad * 2, false);
+            if (st != LITELINEAR_OK) return st;
+            p.t_ws2 = h->t_ws2;
+        }
         p.t_splits = ll::tiled_t_splits(p, mc, h->opt_t_splits);
         if (p.t_splits > 1) {
             st = grow((void **)&h->t_part, &h->t_part_bytes, (size_t)p.t_splits * M * r_pad * sizeof(float), false);
@@ -410,9 +451,58 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
         p.t_target = (h->tiled_epoch + 1u) * ll::tiled_flag_step(p, mc);
     }
     st = timed_launch(h, LITELINEAR_KERNEL_MAIN, stream,
-                      [&] { return ll::launch_tiled(p, mc, a_eff, h->tile_sync, stream); });
+                      [&] { return ll::launch_tiled(p, mc, a_eff, a_eff2, h->tile_sync, stream); });
     if (st == LITELINEAR_OK && r > 0) ++h->tiled_epoch;
     return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, const void *A, const void *B,
+                                       const void *Q, float scale, const void *bias, void *y, int64_t M,
+                                       int64_t in, int64_t out, int64_t r, hipStream_t stream) {
+    if (!h) return LITELINEAR_ERR_INVALID_ARG;
+    const bool out_f32 = h->opt_out_f32 != 0;
+    litelinear_status_t st = litelinear_check_args(x, A, B, Q, bias, y, M, in, out, r, out_f32 ? 4 : 2);
+    if (st != LITELINEAR_OK) return st;
+    if (M == 0 || out == 0) return LITELINEAR_OK;
+    DeviceGuard guard(h->device);
+    if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
+    return forward_impl(h, x, B, OutSet{A, Q, bias, scale, y, out}, nullptr, M, in, r, stream);
+}
+
+litelinear_status_t litelinear_forward_pair(litelinear_handle_t h, const void *x, const void *B, const void *A1,
+                                            const void *Q1, float scale1, const void *bias1, void *y1, int64_t out1,
+                                            const void *A2, const void *Q2, float scale2, const void *bias2, void *y2,
+                                            int64_t out2, int64_t M, int64_t in, int64_t r, hipStream_t stream) {
+    if (!h) return LITELINEAR_ERR_INVALID_ARG;
+    const int ysz = h->opt_out_f32 != 0 ? 4 : 2;
+    litelinear_status_t st = litelinear_check_args(x, A1, B, Q1, bias1, y1, M, in, out1, r, ysz);
+    if (st != LITELINEAR_OK) return st;
+    st = litelinear_check_args(x, A2, B, Q2, bias2, y2, M, in, out2, r, ysz);
+    if (st != LITELINEAR_OK) return st;
+    // Each y must also stay clear of the other output's tensors.
+    const uint64_t ny1 = (uint64_t)M * (uint64_t)out1 * ysz, ny2 = (uint64_t)M * (uint64_t)out2 * ysz;
+    if (overlaps(y1, ny1, y2, ny2) || overlaps(y1, ny1, Q2, (uint64_t)out2 * in) ||
+        overlaps(y1, ny1, bias2, (uint64_t)out2 * 2) || overlaps(y2, ny2, Q1, (uint64_t)out1 * in) ||
+        overlaps(y2, ny2, bias1, (uint64_t)out1 * 2) ||
+        (r > 0 && (overlaps(y1, ny1, A2, (uint64_t)out2 * r * 2) || overlaps(y2, ny2, A1, (uint64_t)out1 * r * 2))))
+        return LITELINEAR_ERR_INVALID_ARG;
+    if (M == 0 || (out1 == 0 && out2 == 0)) return LITELINEAR_OK;
+    DeviceGuard guard(h->device);
+    if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
+    const OutSet s1{A1, Q1, bias1, scale1, y1, out1}, s2{A2, Q2, bias2, scale2, y2, out2};
+    // One output empty, or the skinny regime (where T is a small part of
+    // the time): one forward per output.  Otherwise one tiled launch.
+    const bool skinny = h->opt_path == 1 || (h->opt_path == 0 && M <= kSkinnyAutoMaxM && h->opt_act_fp8 == 0);
+    if (out1 == 0 || out2 == 0 || in == 0 || skinny) {
+        if (out1 > 0 && (st = forward_impl(h, x, B, s1, nullptr, M, in, r, stream)) != LITELINEAR_OK) return st;
+        if (out2 > 0) st = forward_impl(h, x, B, s2, nullptr, M, in, r, stream);
+        return st;
+    }
+    return forward_impl(h, x, B, s1, &s2, M, in, r, stream);
 }
 
 litelinear_status_t litelinear_quantize_rows(litelinear_handle_t h, const void *x, int64_t M, int64_t in,

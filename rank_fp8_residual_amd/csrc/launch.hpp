@@ -24,6 +24,13 @@ struct TiledProblem {
     // product reads these, T still reads x.
     const void *xq;
     const float *xs;
+    // Optional second output sharing x and B (N2 > 0): its Q [N2, K], A
+    // [N2, r], bias, scale and y [M, N2], and a second T' workspace.
+    const void *Q2, *A2, *bias2;
+    void *y2;
+    void *t_ws2;
+    float scale2;
+    int64_t N2;
 };
 
 // x bf16 [M, K] (K % 8 == 0) -> e4m3fn codes [M, K] and one power-of-two
@@ -70,7 +77,8 @@ unsigned tiled_flag_step(const TiledProblem &p, TileCfg c);
 // Columns of T per producer block (64, or 256 for ranks that are multiples
 // of 256 with 256-wide output tiles).
 int tiled_t_cols(const TiledProblem &p, TileCfg c);
-hipError_t launch_tiled(const TiledProblem &p, TileCfg c, const void *a_eff, unsigned *sync, hipStream_t s);
+hipError_t launch_tiled(const TiledProblem &p, TileCfg c, const void *a_eff, const void *a_eff2, unsigned *sync,
+                        hipStream_t s);
 
 // Skinny path (M <= 64): T producers plus output work-groups of 128
 // columns over K slices (see skinny.hip).

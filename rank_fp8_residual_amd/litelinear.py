@@ -56,7 +56,7 @@ class Kernel(enum.IntEnum):
 EXPORTS = ("litelinear_create", "litelinear_forward", "litelinear_destroy", "litelinear_check_args",
            "litelinear_set_option", "litelinear_kernel_time", "litelinear_status_string",
            "litelinear_version", "litelinear_quantize_rows", "litelinear_quantize_tensor",
-           "litelinear_residual_quantize")
+           "litelinear_residual_quantize", "litelinear_forward_pair")
 
 
 class LiteLinearError(RuntimeError):
@@ -98,6 +98,9 @@ def lib(path: str | None = None) -> ctypes.CDLL:
         L.litelinear_quantize_tensor.restype = ctypes.c_int
         L.litelinear_residual_quantize.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
         L.litelinear_residual_quantize.restype = ctypes.c_int
+        L.litelinear_forward_pair.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, i64, vp, vp,
+                                              ctypes.c_float, vp, vp, i64, i64, i64, i64, vp]
+        L.litelinear_forward_pair.restype = ctypes.c_int
         L.litelinear_version.argtypes = []
         L.litelinear_version.restype = ctypes.c_char_p
         if path is None:
@@ -197,6 +200,60 @@ class Handle:
                                       out_features, r, s)
         _check(st, "litelinear_forward")
         return out.view(*lead, out_features)
+
+    def forward_pair(self, x: torch.Tensor, B: torch.Tensor | None, first: tuple, second: tuple,
+                     out: tuple | None = None, stream: torch.cuda.Stream | None = None):
+        """Two outputs sharing x and B (T computed once): `first` and `second`
+        are (A, Q, scale, bias) tuples; returns (y1, y2)."""
+        dev = self.device
+        _expect(x, "x", torch.bfloat16, dev, None)
+        in_features = x.shape[-1]
+        lead = x.shape[:-1]
+        x2 = x.reshape(math.prod(lead), in_features)
+        if not x2.is_contiguous():
+            raise ValueError("x must be contiguous")
+        M = x2.shape[0]
+        r = 0 if B is None else B.shape[0]
+        if B is not None:
+            _expect(B, "B", torch.bfloat16, dev, 2)
+            if B.shape[1] != in_features:
+                raise ValueError("B does not match x")
+        sets = []
+        for name, (A, Q, scale, bias) in (("first", first), ("second", second)):
+            if Q.dtype == torch.float8_e4m3fn:
+                Q = Q.view(torch.uint8)
+            _expect(Q, f"{name} Q", torch.uint8, dev, 2)
+            n_out = Q.shape[0]
+            if Q.shape[1] != in_features:
+                raise ValueError(f"{name} Q does not match x")
+            if (A is None) != (B is None):
+                raise ValueError("A must be given exactly when B is")
+            if A is not None:
+                _expect(A, f"{name} A", torch.bfloat16, dev, 2)
+                if A.shape != (n_out, r):
+                    raise ValueError(f"{name} A must be [{n_out}, {r}]")
+            if bias is not None:
+                _expect(bias, f"{name} bias", torch.bfloat16, dev, 1)
+                if bias.shape[0] != n_out:
+                    raise ValueError(f"{name} bias must have {n_out} elements")
+            sets.append((A, Q, float(scale), bias, n_out))
+        ydt = torch.float32 if self.out_f32 else torch.bfloat16
+        ys = []
+        for i, (_, _, _, _, n_out) in enumerate(sets):
+            y = out[i] if out is not None else torch.empty((M, n_out), dtype=ydt, device=dev)
+            _expect(y, "out", ydt, dev, None)
+            if y.numel() != M * n_out:
+                raise ValueError("out has the wrong number of elements")
+            ys.append(y)
+        s = (stream or torch.cuda.current_stream(dev)).cuda_stream
+        ptr = lambda t: None if t is None or t.numel() == 0 else t.data_ptr()
+        (A1, Q1, s1, b1, n1), (A2, Q2, s2, b2, n2) = sets
+        st = lib().litelinear_forward_pair(self._h, ptr(x2), ptr(B) if r else None, ptr(A1) if r else None, ptr(Q1),
+                                           ctypes.c_float(s1), ptr(b1), ptr(ys[0]), n1,
+                                           ptr(A2) if r else None, ptr(Q2), ctypes.c_float(s2), ptr(b2), ptr(ys[1]),
+                                           n2, M, in_features, r, s)
+        _check(st, "litelinear_forward_pair")
+        return ys[0].view(*lead, n1), ys[1].view(*lead, n2)
 
     def quantize_rows(self, x: torch.Tensor, codes: torch.Tensor | None = None,
                       scales: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
