@@ -31,6 +31,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -49,6 +50,7 @@ KERNEL_NAMES = {"main": "fused_kernel", "pad_a": "pad_rows_kernel", "skinny": "s
 ACT8_SUMMARY = ("llm", "dit_r32", "dit_r64", "dit_r512", "large")
 # weights whose decomposition step (residual + e4m3fn quantisation) is timed
 CONVERT_SUMMARY = ("dit_r64", "large")
+PAIR_SUMMARY = ("llm", "dit_r64")  # shared-B pairs of these shapes
 HEADLINE = "dit_r64"
 
 
@@ -314,8 +316,10 @@ def main():
             key = "convert+" + name
             summary[key] = convert_timing(wl.WORKLOADS[name], dev)
             log(key, summary[key])
-        summary["pair+dit_r64"] = pair_timing(wl.WORKLOADS["dit_r64"], args, dev)
-        log("pair+dit_r64", summary["pair+dit_r64"])
+        for name in PAIR_SUMMARY:
+            key = "pair+" + name
+            summary[key] = pair_timing(wl.WORKLOADS[name], args, dev)
+            log(key, summary[key])
 
     if args.copy_probe:
         copy_probe(dev)
@@ -373,18 +377,24 @@ def pair_timing(w, args, dev, steps=100):
                                   (g2["A"], g2["Q"], g2["scale"], g2["bias"]), out=(y1, y2))
     two = lambda: (h.forward(g1["x"], g1["A"], g1["B"], g1["Q"], g1["scale"], g1["bias"], out=y1),
                    h.forward(g2["x"], g2["A"], g2["B"], g2["Q"], g2["scale"], g2["bias"], out=y2))
-    res = {}
-    for name, fn in (("pair", pair), ("two_forwards", two)):
-        for _ in range(50):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        res[name + "_us"] = round(e0.elapsed_time(e1) / steps * 1e3, 2)
+    # Blocks of the two variants alternate, so that clock and power drift
+    # over the run falls on both alike; each reports its median block.
+    times = {"pair": [], "two_forwards": []}
+    for _ in range(50):
+        pair()
+        two()
+    torch.cuda.synchronize()
+    block = max(1, steps // 10)
+    for _ in range(10):
+        for name, fn in (("pair", pair), ("two_forwards", two)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(block):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times[name].append(e0.elapsed_time(e1) / block * 1e3)
+    res = {k + "_us": round(statistics.median(v), 2) for k, v in times.items()}
     res["TFLOP/s_pair"] = round(2 * w.flops / (res["pair_us"] * 1e-6) / 1e12, 2)
     res["note"] = "two outputs of this shape sharing x and B; T computed once by the pair"
     return res
