@@ -157,6 +157,27 @@ def test_tiled_t_split_counts(dev, t_splits):
     parity.check(parity.to_f64(y1), y_ref, False)
 
 
+@pytest.mark.parametrize("shape", [(512, 1024, 8192, 64), (890, 768, 4600, 40), (4096, 512, 4096, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("act8", [False, True], ids=["bf16", "act8"])
+def test_tiled_full_round_grids(dev, shape, act8):
+    """Output grids of one full round of work-groups (or nearly), so that the
+    T producers push output tiles into a second round (64- and 256-column T
+    blocks); checked on sampled rows, and repeat calls agree bit for bit."""
+    M, K, N, r = shape
+    d = wl.random_inputs(M, K, N, r, seed=80 + r)
+    say("tiled full round", shape, "act8" if act8 else "bf16")
+    h = make_handle(dev, Path.TILED)
+    h.set_option(Option.ACT_FP8, int(act8))
+    g = to_dev(d, dev)
+    y1 = run(h, g)
+    y2 = run(h, g)
+    assert torch.equal(y1, y2)
+    rows = sample_rows(M, 40)
+    y_ref = oracle.forward(d["x"], d["A"], d["B"], d["Q"], d["scale"], d["bias"], rows=rows, act_fp8=act8)
+    parity.check(parity.to_f64(y1[torch.from_numpy(rows).to(dev)]), y_ref, False)
+
+
 @pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
 def test_bf16_output_is_rne_of_f32_output(dev, path):
     """The bf16 output is the float32 output rounded to nearest even (the
