@@ -45,7 +45,9 @@ typedef enum {
 
 /* Options set per handle with litelinear_set_option(). */
 typedef enum {
-    /* Kernel family.  0 = choose from M (default); 1 = the skinny split-K
+    /* Kernel family.  0 = choose from M (default: skinny for M <= 64, but
+     * for tiny problems, 32 < M, in <= 256 and M * in * out <= 2^22, where
+     * the tiled kernel computes T inside each output tile); 1 = the skinny split-K
      * kernel (HBM-bound on Q, for small M); 2 = the tiled kernel (MFMA-bound,
      * for large M).  Both compute the same operation. */
     LITELINEAR_OPT_PATH = 1,

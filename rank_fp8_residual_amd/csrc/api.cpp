@@ -311,7 +311,7 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, const void *B
     const bool skinny_ok = !act8 && in > 0 && ll::skinny_supports(M) &&
                            ll::skinny_shape_ok(M, in, out, r_pad, plan = ll::skinny_plan(M, in, out, r_pad, h->opt_split));
     if (s2) path = 2;
-    if (path == 0) path = (M <= kSkinnyAutoMaxM && skinny_ok) ? 1 : 2;
+    if (path == 0) path = (M <= kSkinnyAutoMaxM && skinny_ok && !ll::tiled_tiny_shape(M, in, out, r)) ? 1 : 2;
     if (path == 1 && !skinny_ok) return LITELINEAR_ERR_UNSUPPORTED;
 
     // A whose rows are not whole 16-byte chunks is first copied into a
@@ -420,7 +420,10 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, const void *B
         p.xq = h->xq;
         p.xs = h->xs;
     }
-    if (r > 0) {
+    // With producers, T goes through the T' workspace and the row tiles'
+    // ready counters; small problems compute it in each output tile instead.
+    const bool producers = r > 0 && !ll::tiled_self_t(p, mc);
+    if (producers) {
         st = grow(&h->t_ws, &h->t_ws_bytes, (size_t)M * r_pad * 2, false);
         if (st != LITELINEAR_OK) return st;
         p.t_ws = h->t_ws;
@@ -452,7 +455,7 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, const void *B
     }
     st = timed_launch(h, LITELINEAR_KERNEL_MAIN, stream,
                       [&] { return ll::launch_tiled(p, mc, a_eff, a_eff2, h->tile_sync, stream); });
-    if (st == LITELINEAR_OK && r > 0) ++h->tiled_epoch;
+    if (st == LITELINEAR_OK && producers) ++h->tiled_epoch;
     return st;
 }
 

@@ -74,6 +74,12 @@ int tiled_t_splits(const TiledProblem &p, TileCfg c, int64_t hint);
 // Per T block, finished K slices (left at zero by every launch).
 int64_t tiled_sync_words(const TiledProblem &p, TileCfg c);
 unsigned tiled_flag_step(const TiledProblem &p, TileCfg c);
+// True when the output work-groups compute T themselves (no producers, no
+// T workspace or counters): 128 x 128 tiles of tiny, latency-bound problems
+// (tiled_tiny_shape(), which also sends such problems with M <= 64 to the
+// tiled kernel when the path is chosen automatically).
+bool tiled_tiny_shape(int64_t M, int64_t K, int64_t N, int64_t r);
+bool tiled_self_t(const TiledProblem &p, TileCfg c);
 // Columns of T per producer block (64, or 256 for ranks that are multiples
 // of 256 with 256-wide output tiles).
 int tiled_t_cols(const TiledProblem &p, TileCfg c);

@@ -125,7 +125,9 @@ class Handle:
     def __init__(self, device: int | torch.device | None = None):
         if device is None:
             device = torch.cuda.current_device()
-        self.device = torch.device("cuda", device) if isinstance(device, int) else torch.device(device)
+        dev = torch.device("cuda", device) if isinstance(device, int) else torch.device(device)
+        # always with an index: argument checks compare it with get_device()
+        self.device = torch.device("cuda", dev.index if dev.index is not None else torch.cuda.current_device())
         self._h = ctypes.c_void_p()
         _check(lib().litelinear_create(ctypes.byref(self._h), self.device.index or 0), "litelinear_create")
         self.out_f32 = False
@@ -167,9 +169,7 @@ class Handle:
         if x.shape[-1] != in_features:
             raise ValueError(f"x has {x.shape[-1]} features, Q has {in_features}")
         lead = x.shape[:-1]
-        x2 = x.reshape(math.prod(lead), in_features)
-        if not x2.is_contiguous():
-            raise ValueError("x must be contiguous")
+        x2 = x if x.dim() == 2 else x.reshape(math.prod(lead), in_features)
         M = x2.shape[0]
         if A is None or B is None:
             if (A is None) != (B is None):
@@ -193,13 +193,12 @@ class Handle:
             _expect(out, "out", ydt, dev, None)
             if out.numel() != M * out_features:
                 raise ValueError("out has the wrong number of elements")
-        s = (stream or torch.cuda.current_stream(dev)).cuda_stream
-        ptr = lambda t: None if t is None or t.numel() == 0 else t.data_ptr()
-        st = lib().litelinear_forward(self._h, ptr(x2), ptr(A) if r else None, ptr(B) if r else None, ptr(Q),
-                                      ctypes.c_float(float(scale)), ptr(bias), ptr(out), M, in_features,
-                                      out_features, r, s)
-        _check(st, "litelinear_forward")
-        return out.view(*lead, out_features)
+        s = _stream_ptr(stream, dev)
+        st = lib().litelinear_forward(self._h, _ptr(x2), _ptr(A) if r else None, _ptr(B) if r else None, _ptr(Q),
+                                      float(scale), _ptr(bias), _ptr(out), M, in_features, out_features, r, s)
+        if st:
+            _check(st, "litelinear_forward")
+        return out if out.dim() == 2 and len(lead) == 1 else out.view(*lead, out_features)
 
     def forward_pair(self, x: torch.Tensor, B: torch.Tensor | None, first: tuple, second: tuple,
                      out: tuple | None = None, stream: torch.cuda.Stream | None = None):
@@ -245,7 +244,7 @@ class Handle:
             if y.numel() != M * n_out:
                 raise ValueError("out has the wrong number of elements")
             ys.append(y)
-        s = (stream or torch.cuda.current_stream(dev)).cuda_stream
+        s = _stream_ptr(stream, dev)
         ptr = lambda t: None if t is None or t.numel() == 0 else t.data_ptr()
         (A1, Q1, s1, b1, n1), (A2, Q2, s2, b2, n2) = sets
         st = lib().litelinear_forward_pair(self._h, ptr(x2), ptr(B) if r else None, ptr(A1) if r else None, ptr(Q1),
@@ -274,7 +273,7 @@ class Handle:
             _expect(scales, "scales", torch.float32, dev, 1)
             if scales.shape[0] != M:
                 raise ValueError("scales must have one element per row")
-        s = (stream or torch.cuda.current_stream(dev)).cuda_stream
+        s = _stream_ptr(stream, dev)
         ptr = lambda t: None if t.numel() == 0 else t.data_ptr()
         _check(lib().litelinear_quantize_rows(self._h, ptr(x), M, K, ptr(codes), ptr(scales), s),
                "litelinear_quantize_rows")
@@ -287,7 +286,7 @@ class Handle:
         _expect(R, "R", torch.float32, dev, None)
         codes = torch.empty(R.shape, dtype=torch.uint8, device=dev)
         scale = torch.empty((1,), dtype=torch.float32, device=dev)
-        s = (stream or torch.cuda.current_stream(dev)).cuda_stream
+        s = _stream_ptr(stream, dev)
         ptr = lambda t: None if t.numel() == 0 else t.data_ptr()
         _check(lib().litelinear_quantize_tensor(self._h, ptr(R), R.numel(), ptr(codes), scale.data_ptr(), s),
                "litelinear_quantize_tensor")
@@ -312,7 +311,7 @@ class Handle:
                 raise ValueError("A / B do not match W")
         codes = torch.empty((out_features, in_features), dtype=torch.uint8, device=dev)
         scale = torch.empty((1,), dtype=torch.float32, device=dev)
-        s = (stream or torch.cuda.current_stream(dev)).cuda_stream
+        s = _stream_ptr(stream, dev)
         ptr = lambda t: None if t is None or t.numel() == 0 else t.data_ptr()
         _check(lib().litelinear_residual_quantize(self._h, ptr(W), ptr(A) if r else None, ptr(B) if r else None,
                                                   out_features, in_features, r, ptr(codes), scale.data_ptr(), s),
@@ -320,12 +319,28 @@ class Handle:
         return codes, scale
 
 
+def _ptr(t):
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_ptr(stream, dev: torch.device):
+    """The HIP stream to enqueue on: the given one, else torch's current one."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(dev.index)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
 def _expect(t, name, dtype, dev, ndim):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if t.device != dev:
+    if t.get_device() != dev.index:
         raise ValueError(f"{name} is on {t.device}, the handle on {dev}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions")

@@ -178,6 +178,45 @@ def test_tiled_full_round_grids(dev, shape, act8):
     parity.check(parity.to_f64(y1[torch.from_numpy(rows).to(dev)]), y_ref, False)
 
 
+TINY_SHAPES = [(64, 256, 256, 16), (100, 128, 300, 100), (40, 64, 520, 64), (257, 256, 48, 8)]
+
+
+@pytest.mark.parametrize("shape", TINY_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("mode", ["bf16", "f32", "unfolded", "act8"])
+def test_tiled_tiny_problems_compute_t_in_each_tile(dev, shape, mode):
+    """Tiny problems (in <= 256, M in (32, ...], M in out <= 2^22): the output
+    tiles compute T themselves (one or two 64-rank blocks), on the automatic
+    path as well as the forced tiled one; repeat calls agree bit for bit."""
+    M, K, N, r = shape
+    d = wl.random_inputs(M, K, N, r, seed=90 + M)
+    if mode == "unfolded":
+        d["scale"] = 2.0 ** -70
+    act8 = mode == "act8"
+    y_ref = oracle.forward(d["x"], d["A"], d["B"], d["Q"], d["scale"], d["bias"], act_fp8=act8)
+    g = to_dev(d, dev)
+    for path in (Path.AUTO, Path.TILED):
+        say("tiny tiled", shape, mode, path.name)
+        h = make_handle(dev, path, out_f32=mode in ("f32", "unfolded"))
+        h.set_option(Option.ACT_FP8, int(act8))
+        y1 = run(h, g)
+        assert torch.equal(y1, run(h, g))
+        parity.check(parity.to_f64(y1), y_ref, mode in ("f32", "unfolded"))
+
+
+def test_tiled_tiny_pair(dev):
+    d1 = wl.random_inputs(64, 256, 200, 48, seed=95)
+    d2 = wl.random_inputs(64, 256, 136, 48, seed=96)
+    d2["x"], d2["B"], d2["scale"] = d1["x"], d1["B"], d1["scale"] * 3.0
+    g1, g2 = to_dev(d1, dev), to_dev(d2, dev)
+    say("tiny tiled pair")
+    h = make_handle(dev, Path.TILED)
+    y1, y2 = h.forward_pair(g1["x"], g1["B"], (g1["A"], g1["Q"], g1["scale"], g1["bias"]),
+                            (g2["A"], g2["Q"], g2["scale"], g2["bias"]))
+    torch.cuda.synchronize()
+    parity.check(parity.to_f64(y1), oracle_y(d1), False)
+    parity.check(parity.to_f64(y2), oracle_y(d2), False)
+
+
 @pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
 def test_bf16_output_is_rne_of_f32_output(dev, path):
     """The bf16 output is the float32 output rounded to nearest even (the
