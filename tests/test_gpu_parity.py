@@ -264,14 +264,16 @@ def test_wide_t_blocks(dev, r):
 def test_handle_reuse_across_shapes(dev, path):
     """One handle, a sequence of shapes that change the column-tile count,
     the row-tile count, the rank (and so the T flag step), with r = 0 calls
-    in between: every call must match the oracle (the handle's counters
-    are restarted whenever their layout changes)."""
+    and tiny problems (T computed in each output tile, counters untouched) in
+    between: every call must match the oracle (the handle's counters are
+    restarted whenever their layout changes)."""
     if path == Path.SKINNY:
         shapes = [(16, 512, 256, 64), (16, 512, 1024, 64), (16, 512, 1024, 0), (16, 512, 256, 64),
                   (16, 512, 256, 128), (9, 1024, 2176, 64), (16, 512, 256, 64)]
     else:
-        shapes = [(300, 256, 512, 64), (600, 256, 512, 64), (300, 256, 512, 128), (300, 256, 512, 0),
-                  (300, 256, 512, 64), (700, 512, 384, 192), (300, 256, 512, 64)]
+        shapes = [(300, 256, 512, 64), (300, 128, 100, 64), (600, 256, 512, 64), (300, 256, 512, 128),
+                  (300, 256, 512, 0), (64, 256, 256, 16), (300, 256, 512, 64), (700, 512, 384, 192),
+                  (300, 128, 100, 64), (300, 256, 512, 64)]
     h = make_handle(dev, path)
     cache = {}
     for rep in range(2):
