@@ -71,12 +71,6 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(unsigned, v);
 }
 
-__device__ __forceinline__ u32x4 load16(const void *p) {
-    return *reinterpret_cast<const u32x4 *>(p);
-}
-
-__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
-
 // ---- buffer (descriptor-based) loads: an offset at or past the descriptor's
 // byte count reads as zero, so masking needs no branch.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
