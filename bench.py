@@ -255,8 +255,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} / WORLD_SIZE {world} is not supported "
-              "(every MI355X box here has one GPU; the forward's rows shard with no communication, "
-              "so N GPUs give N times this figure)", file=sys.stderr)
+              "(the forward's rows shard across GPUs with no communication, so N GPUs give N times "
+              "the one-GPU figure)", file=sys.stderr)
         sys.exit(2)
 
     import torch
