@@ -351,9 +351,35 @@ def main():
         },
         "roofline": roof,
         "cpu_baseline": cpu,
+        "device": device_info(dev),
         "workloads": summary,
     }
     print(json.dumps(line), flush=True)
+
+
+def device_info(dev) -> dict:
+    """Name, architecture, compute units and peak clocks of the device."""
+    import ctypes
+
+    import torch
+
+    p = torch.cuda.get_device_properties(dev)
+    info = {"name": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count}
+    from rank_fp8_residual_amd import litelinear as L
+
+    try:
+        # the HIP runtime the library itself is linked against (symbol lookup
+        # through its handle searches its dependencies)
+        get_attr = L.lib().hipDeviceGetAttribute
+    except AttributeError:
+        return info
+    # hipDeviceAttributeClockRate and hipDeviceAttributeMemoryClockRate
+    # (hip_runtime_api.h, ROCm 7), both in kHz
+    for key, attr in (("peak_clock_mhz", 5), ("memory_clock_mhz", 60)):
+        v = ctypes.c_int()
+        if get_attr(ctypes.byref(v), attr, dev.index) == 0:
+            info[key] = v.value // 1000
+    return info
 
 
 def pair_timing(w, args, dev, steps=100):
