@@ -111,9 +111,10 @@ struct RArgs {
 template <bool QUANT>
 __global__ void __launch_bounds__(R_THREADS) residual_kernel(RArgs a) {
     // B's step tile transposed: bt[j][k], 32 ranks (64 bytes) per column,
-    // rows padded by 16 bytes so the fragment reads spread over the banks.
+    // rows padded by 16 bytes so the fragment reads spread over the banks;
+    // two of them, for alternate steps.
     constexpr int BTS = RK * 2 + 16;
-    __shared__ __attribute__((aligned(16))) unsigned char bt[RT * BTS];
+    __shared__ __attribute__((aligned(16))) unsigned char bt[2 * RT * BTS];
     __shared__ unsigned red[R_THREADS / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
     const int tiles_k = (a.K + RT - 1) / RT;
@@ -146,46 +147,61 @@ __global__ void __launch_bounds__(R_THREADS) residual_kernel(RArgs a) {
 #pragma unroll
         for (int fr = 0; fr < 2; ++fr) acc[fc][fr] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int k0 = 0; k0 < a.r; k0 += RK) {
-        // B tile: thread t loads ranks k0 + 4 (t / 32) .. +4 of columns
-        // j0 + 4 (t % 32) .. +4 (four 8-byte loads, 256 contiguous bytes per
-        // rank row across 32 lanes) and writes each column's four ranks to
-        // bt as one 8-byte store.
-        {
-            const int kq = 4 * (tid >> 5), jq = 4 * (tid & 31), j = j0 + jq;
-            u32x2 v[4];
+    // B tile of a step: thread t loads ranks k0 + 4 (t / 32) .. +4 of columns
+    // j0 + 4 (t % 32) .. +4 (four 8-byte loads, 256 contiguous bytes per rank
+    // row across 32 lanes); A fragments: 16 bytes per row block.  The loads
+    // of step k + 1 are in flight while step k is transposed and multiplied.
+    const int kq = 4 * (tid >> 5), jq = 4 * (tid & 31), jb = j0 + jq;
+    auto load_b = [&](int k0, u32x2 (&v)[4]) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int k = k0 + kq + e;
-                v[e] = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                               rb, ((unsigned)k * (unsigned)a.K + (unsigned)j) * 2u + (k < a.r && j < a.K ? 0u : kOOB),
-                               0, 0));
-            }
-            __syncthreads();  // the previous step's fragments have been read
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                // column jq + c: ranks kq .. kq + 3 = element c of each row load
-                const unsigned lo = c & 1 ? (v[0][c >> 1] >> 16) | (v[1][c >> 1] & 0xFFFF0000u)
-                                          : (v[0][c >> 1] & 0xFFFFu) | (v[1][c >> 1] << 16);
-                const unsigned hi = c & 1 ? (v[2][c >> 1] >> 16) | (v[3][c >> 1] & 0xFFFF0000u)
-                                          : (v[2][c >> 1] & 0xFFFFu) | (v[3][c >> 1] << 16);
-                *reinterpret_cast<u32x2 *>(bt + (jq + c) * BTS + kq * 2) = u32x2{lo, hi};
-            }
-            __syncthreads();
+        for (int e = 0; e < 4; ++e) {
+            const int k = k0 + kq + e;
+            v[e] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                           rb, ((unsigned)k * (unsigned)a.K + (unsigned)jb) * 2u + (k < a.r && jb < a.K ? 0u : kOOB),
+                           0, 0));
         }
-        u32x4 af[2];
+    };
+    auto load_a = [&](int k0, u32x4 (&af)[2]) {
 #pragma unroll
         for (int fr = 0; fr < 2; ++fr) {
             const int n = n0 + 32 * wave + 16 * fr + l16, k = k0 + 8 * g;
             af[fr] = bload16(ra, ((unsigned)n * (unsigned)a.r + (unsigned)k) * 2u + (n < a.N && k < a.r ? 0u : kOOB));
         }
+    };
+    u32x2 bv[4], bn[4];
+    u32x4 af[2], an[2];
+    if (a.r > 0) {
+        load_b(0, bv);
+        load_a(0, af);
+    }
+    for (int k0 = 0, st = 0; k0 < a.r; k0 += RK, st ^= 1) {
+        if (k0 + RK < a.r) {
+            load_b(k0 + RK, bn);
+            load_a(k0 + RK, an);
+        }
+        // bt[st] was last read two steps ago, before the previous step's barrier.
+        unsigned char *const b = bt + st * (RT * BTS);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            // column jq + c: ranks kq .. kq + 3 = element c of each row load
+            const unsigned lo = c & 1 ? (bv[0][c >> 1] >> 16) | (bv[1][c >> 1] & 0xFFFF0000u)
+                                      : (bv[0][c >> 1] & 0xFFFFu) | (bv[1][c >> 1] << 16);
+            const unsigned hi = c & 1 ? (bv[2][c >> 1] >> 16) | (bv[3][c >> 1] & 0xFFFF0000u)
+                                      : (bv[2][c >> 1] & 0xFFFFu) | (bv[3][c >> 1] << 16);
+            *reinterpret_cast<u32x2 *>(b + (jq + c) * BTS + kq * 2) = u32x2{lo, hi};
+        }
+        __syncthreads();
 #pragma unroll
         for (int fc = 0; fc < RT / 16; ++fc) {
-            const u32x4 bf = *reinterpret_cast<const u32x4 *>(bt + (16 * fc + l16) * BTS + 16 * g);
+            const u32x4 bf = *reinterpret_cast<const u32x4 *>(b + (16 * fc + l16) * BTS + 16 * g);
 #pragma unroll
             for (int fr = 0; fr < 2; ++fr) acc[fc][fr] = mfma16(bf, af[fr], acc[fc][fr]);
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[e] = bn[e];
+        af[0] = an[0];
+        af[1] = an[1];
     }
 
     // R = W - A B for the lane's elements: row n, columns j .. j + 3.
