@@ -173,7 +173,7 @@ litelinear_status_t litelinear_quantize_rows(litelinear_handle_t h, const void *
  *   W      bf16 [out, in] 16-byte aligned, in % 16 == 0.
  *   A      bf16 [out, r]  16-byte aligned, r % 8 == 0 (may be NULL iff r == 0).
  *   B      bf16 [r, in]   16-byte aligned (may be NULL iff r == 0).
- *   codes  uint8 [out, in] 4-byte aligned; scale_out as above.
+ *   codes  uint8 [out, in] 16-byte aligned; scale_out as above.
  *
  * Both read their input twice (max |R|, then the codes), use one word of
  * the handle's workspace, and are queued on `stream`.  Outputs must not

@@ -560,7 +560,7 @@ litelinear_status_t litelinear_residual_quantize(litelinear_handle_t h, const vo
     if (!scale_out) return LITELINEAR_ERR_INVALID_ARG;
     if (out > 0 && in > 0 && (!W || !codes || (r > 0 && (!A || !B)))) return LITELINEAR_ERR_INVALID_ARG;
     if (in % 16 != 0 || r % 8 != 0) return LITELINEAR_ERR_UNSUPPORTED;
-    if (!aligned(scale_out, 4) || (out > 0 && in > 0 && (!aligned(W, 16) || !aligned(codes, 4))) ||
+    if (!aligned(scale_out, 4) || (out > 0 && in > 0 && (!aligned(W, 16) || !aligned(codes, 16))) ||
         (r > 0 && out > 0 && in > 0 && (!aligned(A, 16) || !aligned(B, 16))))
         return LITELINEAR_ERR_UNSUPPORTED;
     const int64_t l31 = (int64_t)1 << 31;

@@ -115,6 +115,12 @@ __global__ void __launch_bounds__(R_THREADS) residual_kernel(RArgs a) {
     // two of them, for alternate steps.
     constexpr int BTS = RK * 2 + 16;
     __shared__ __attribute__((aligned(16))) unsigned char bt[2 * RT * BTS];
+    // The W tile (rows of RT bf16) and then the tile's codes (rows of RT
+    // bytes), both with rows padded by 16 bytes: memory sees whole row
+    // segments in 16-byte lanes, the fragments read and write them through
+    // LDS (the 16 rows of a fragment fall on distinct banks).
+    constexpr int WS = RT * 2 + 16, CS = RT + 16;
+    __shared__ __attribute__((aligned(16))) unsigned char ws[RT * WS];
     __shared__ unsigned red[R_THREADS / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
     const int tiles_k = (a.K + RT - 1) / RT;
@@ -123,21 +129,17 @@ __global__ void __launch_bounds__(R_THREADS) residual_kernel(RArgs a) {
     const rsrc_t rb = make_rsrc(a.B, (int64_t)a.r * a.K * 2);
     const rsrc_t rw = make_rsrc(a.W, (int64_t)a.N * a.K * 2);
 
-    // The lane's W elements (row n, columns j .. j + 3 of each fragment pair)
-    // are requested first, as 8-byte loads, and land while A B is summed.
-    u32x2 wv[2][RT / 16];
+    // The W tile is requested first, 16 bytes per lane along rows (16 lanes
+    // per 256-byte row segment, 16 rows per round), and lands while A B is
+    // summed.  Rows past N and columns past K read as zero.
+    constexpr int WROUNDS = RT * RT * 2 / (16 * R_THREADS);
+    const int wrow = tid >> 4, wcol = 8 * (tid & 15);
+    u32x4 wl[WROUNDS];
 #pragma unroll
-    for (int fr = 0; fr < 2; ++fr) {
-        const int n = n0 + 32 * wave + 16 * fr + l16;
-#pragma unroll
-        for (int fc = 0; fc < RT / 16; ++fc) {
-            const int j = j0 + 16 * fc + 4 * g;
-            const bool ok = n < a.N && j < a.K;  // K % 16 == 0: all four columns or none
-            wv[fr][fc] = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, ((unsigned)n * (unsigned)a.K + (unsigned)j) * 2u +
-                                                                    (ok ? 0u : kOOB),
-                                                            0, 0));
-        }
+    for (int p = 0; p < WROUNDS; ++p) {
+        const int n = n0 + 16 * p + wrow, j = j0 + wcol;
+        const bool ok = n < a.N && j < a.K;  // K % 16 == 0: all eight columns or none
+        wl[p] = bload16(rw, ((unsigned)n * (unsigned)a.K + (unsigned)j) * 2u + (ok ? 0u : kOOB));
     }
 
     // acc[fc][fr]: lane holds (A B)[n0 + 32 wave + 16 fr + l16][j0 + 16 fc + 4 g + v]
@@ -204,40 +206,61 @@ __global__ void __launch_bounds__(R_THREADS) residual_kernel(RArgs a) {
         af[1] = an[1];
     }
 
-    // R = W - A B for the lane's elements: row n, columns j .. j + 3.
+#pragma unroll
+    for (int p = 0; p < WROUNDS; ++p) *reinterpret_cast<u32x4 *>(ws + (16 * p + wrow) * WS + 2 * wcol) = wl[p];
+    __syncthreads();
+
+    // R = W - A B for the lane's elements: row 32 wave + 16 fr + l16 of the
+    // tile, columns 16 fc + 4 g .. + 3.
     float s = 1.0f, m = 0.0f;
     if (QUANT) {
         s = scale_of(a.amax_bits);
         if (blockIdx.x == 0 && tid == 0) *a.scale_out = s;
     }
+    unsigned cv[2][RT / 16];
 #pragma unroll
     for (int fr = 0; fr < 2; ++fr) {
-        const int n = n0 + 32 * wave + 16 * fr + l16;
+        const int row = 32 * wave + 16 * fr + l16;
+        const bool okn = n0 + row < a.N;
 #pragma unroll
         for (int fc = 0; fc < RT / 16; ++fc) {
-            const int j = j0 + 16 * fc + 4 * g;
-            const bool okn = n < a.N;
+            const int col = 16 * fc + 4 * g;
+            const bool ok = okn && j0 + col < a.K;
+            const u32x2 w4 = *reinterpret_cast<const u32x2 *>(ws + row * WS + 2 * col);
             float rv[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const float w = bf16_to_f32((unsigned short)(wv[fr][fc][v >> 1] >> (16 * (v & 1))));
-                rv[v] = (okn && j < a.K) ? w - acc[fc][fr][v] : 0.0f;
+                const float w = bf16_to_f32((unsigned short)(w4[v >> 1] >> (16 * (v & 1))));
+                rv[v] = ok ? w - acc[fc][fr][v] : 0.0f;
             }
-            if (!QUANT) {
+            if (!QUANT)
                 m = fmaxf(m, fmaxf(fmaxf(fabsf(rv[0]), fabsf(rv[1])), fmaxf(fabsf(rv[2]), fabsf(rv[3]))));
-            } else if (okn && j < a.K) {
-                const unsigned c =
-                    codes4(clamp448(rv[0] / s), clamp448(rv[1] / s), clamp448(rv[2] / s), clamp448(rv[3] / s));
-                unsigned char *dst = a.codes + (int64_t)n * a.K + j;
-                if (j + 3 < a.K) {
-                    *reinterpret_cast<unsigned *>(dst) = c;
-                } else {
-                    for (int v = 0; v < 4 && j + v < a.K; ++v) dst[v] = (unsigned char)(c >> (8 * v));
-                }
-            }
+            else
+                cv[fr][fc] = codes4(clamp448(rv[0] / s), clamp448(rv[1] / s), clamp448(rv[2] / s), clamp448(rv[3] / s));
         }
     }
-    if (!QUANT) wg_max(m, a.amax_bits, red, R_THREADS / 64);
+    if (!QUANT) {
+        wg_max(m, a.amax_bits, red, R_THREADS / 64);
+        return;
+    }
+    // Codes: into LDS in fragment order (over the W tile, once every wave
+    // has read it), then out in whole 128-byte row segments.
+    __syncthreads();
+#pragma unroll
+    for (int fr = 0; fr < 2; ++fr)
+#pragma unroll
+        for (int fc = 0; fc < RT / 16; ++fc)
+            *reinterpret_cast<unsigned *>(ws + (32 * wave + 16 * fr + l16) * CS + 16 * fc + 4 * g) = cv[fr][fc];
+    __syncthreads();
+    constexpr int CROUNDS = RT * RT / (16 * R_THREADS);
+    const int crow = tid >> 3, ccol = 16 * (tid & 7);
+#pragma unroll
+    for (int p = 0; p < CROUNDS; ++p) {
+        const int row = 32 * p + crow, n = n0 + row, j = j0 + ccol;
+        const u32x4 c = *reinterpret_cast<const u32x4 *>(ws + row * CS + ccol);
+        if (n < a.N && j < a.K)  // K % 16 == 0: all sixteen codes or none
+            *reinterpret_cast<u32x4 *>(a.codes + (int64_t)n * a.K + j) = c;
+    }
 }
 
 }  // namespace
