@@ -178,6 +178,28 @@ def test_tiled_full_round_grids(dev, shape, act8):
     parity.check(parity.to_f64(y1[torch.from_numpy(rows).to(dev)]), y_ref, False)
 
 
+@pytest.mark.parametrize("shape", [(2000, 1008, 4000, 48), (2304, 2064, 3968, 64), (2048, 48, 4096, 16),
+                                   (1800, 16, 4100, 8), (2048, 4096, 4096, 64)], ids=lambda s: "x".join(map(str, s)))
+def test_tiled_256x128_tiles(dev, shape):
+    """Grids of 256 x 128 output tiles (at least 256 of them, fewer than 256
+    of 256 x 256): K ends 16 or 48 elements into a 64-element step, or on
+    one (for in = 16 and 48 the only step is that partial one), with ragged
+    row and column tiles; sampled rows of every row tile, and repeat calls
+    agree bit for bit."""
+    M, K, N, r = shape
+    assert -(-M // 256) * -(-N // 128) >= 256 > -(-M // 256) * -(-N // 256)
+    d = wl.random_inputs(M, K, N, r, seed=90 + r)
+    say("tiled 256x128", shape)
+    h = make_handle(dev, Path.TILED)
+    g = to_dev(d, dev)
+    y1 = run(h, g)
+    y2 = run(h, g)
+    assert torch.equal(y1, y2)
+    rows = sample_rows(M, 40)
+    y_ref = oracle.forward(d["x"], d["A"], d["B"], d["Q"], d["scale"], d["bias"], rows=rows)
+    parity.check(parity.to_f64(y1[torch.from_numpy(rows).to(dev)]), y_ref, False)
+
+
 TINY_SHAPES = [(64, 256, 256, 16), (100, 128, 300, 100), (40, 64, 520, 64), (257, 256, 48, 8)]
 
 
