@@ -161,6 +161,20 @@ __device__ __forceinline__ void barrier_lds() {
     asm volatile("" ::: "memory");
 }
 
+// Waits until this wave's LDS reads and writes have completed.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Work-group barrier that the instruction scheduler moves nothing across
+// (neither memory accesses nor arithmetic), for code whose phases between
+// barriers are chosen on purpose.
+__device__ __forceinline__ void pp_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // barrier_lds after this wave's own LDS reads and writes have completed
 // (lgkmcnt 0): LDS written before it by any wave is what reads after it see.
 __device__ __forceinline__ void barrier_lds_sync() {
