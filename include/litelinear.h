@@ -80,7 +80,18 @@ typedef enum {
      * element-wise and within 2.4e-2 in relative L1; its tests allow 0.25
      * RMS(y) and 4e-2.  Runs on the tiled kernel only (with
      * LITELINEAR_OPT_PATH = 1 the forward returns UNSUPPORTED). */
-    LITELINEAR_OPT_ACT_FP8 = 6
+    LITELINEAR_OPT_ACT_FP8 = 6,
+    /* Activation fused into the epilogue, for activation projections such
+     * as the feed-forward input projections of the LTX-Video transformer
+     * whose shapes the LiteLinear README benchmarks (*Performance Benchmark
+     * on shapes captured from LTX-Video*).  0 = none (default); 1 = GELU in
+     * its tanh approximation (Hendrycks and Gimpel, "Gaussian Error Linear
+     * Units (GELUs)", 2016) applied to every element of y after the bias:
+     *     y = gelu(v) = 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))),
+     * v the forward's float32 value, before the one rounding to bf16 (or
+     * none with LITELINEAR_OPT_OUTPUT_F32).  Both paths, the fp8-activation
+     * mode and both outputs of litelinear_forward_pair(). */
+    LITELINEAR_OPT_ACTIVATION = 7
 } litelinear_option_t;
 
 /* Kernels whose time litelinear_kernel_time() reports. */

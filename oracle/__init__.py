@@ -136,6 +136,16 @@ def quantize_tensor(R, lib=None):
     return codes, float(np.float32(s))
 
 
+def gelu_tanh(v) -> np.ndarray:
+    """GELU in its tanh approximation, in float64 (Hendrycks and Gimpel,
+    "Gaussian Error Linear Units (GELUs)", 2016, section 2):
+    0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).  The activation that the
+    library's activation option fuses into its epilogue, applied here to the
+    oracle's float64 forward."""
+    v = np.asarray(v, dtype=np.float64)
+    return 0.5 * v * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (v + 0.044715 * v ** 3)))
+
+
 def forward(x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,
             Q: torch.Tensor, scale: float, bias: torch.Tensor | None,
             rows=None, threads: int | None = None, want_T: bool = False, lib=None,

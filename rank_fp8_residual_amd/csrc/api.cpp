@@ -80,7 +80,7 @@ struct litelinear_ctx {
     size_t xs_bytes = 0;
     unsigned *amax = nullptr;       // decomposition side: max |R| as float bits
     size_t amax_bytes = 0;
-    int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0, opt_t_splits = 0, opt_act_fp8 = 0;
+    int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0, opt_t_splits = 0, opt_act_fp8 = 0, opt_gelu = 0;
     Prof prof[kNumKernels];
     std::vector<hipEvent_t> event_pool;
 };
@@ -251,6 +251,10 @@ litelinear_status_t litelinear_set_option(litelinear_handle_t h, int key, int64_
             if (value != 0 && value != 1) return LITELINEAR_ERR_INVALID_ARG;
             h->opt_act_fp8 = value;
             return LITELINEAR_OK;
+        case LITELINEAR_OPT_ACTIVATION:
+            if (value != 0 && value != 1) return LITELINEAR_ERR_INVALID_ARG;
+            h->opt_gelu = value;
+            return LITELINEAR_OK;
     }
     return LITELINEAR_ERR_INVALID_ARG;
 }
@@ -351,6 +355,7 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, const void *B
         p.r = r;
         p.r_pad = r_pad;
         p.out_f32 = out_f32;
+        p.gelu = h->opt_gelu != 0;
         if (p.plan.splits > 1) {
             st = grow((void **)&h->partials, &h->partials_bytes, (size_t)p.plan.splits * M * out * sizeof(float),
                       false);
@@ -399,6 +404,7 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, const void *B
     p.r = r;
     p.r_pad = r_pad;
     p.out_f32 = out_f32;
+    p.gelu = h->opt_gelu != 0;
     if (s2) {
         p.Q2 = s2->Q;
         p.A2 = s2->A;

@@ -55,6 +55,17 @@ __device__ __forceinline__ void fp8x16_to_bf16x16(u32x4 q, u32x4 &h0, u32x4 &h1)
     h1 = u32x4{c.x, c.y, d.x, d.y};
 }
 
+// GELU in its tanh approximation (Hendrycks and Gimpel, "Gaussian Error
+// Linear Units (GELUs)", 2016): 0.5 v (1 + tanh(u)), u = sqrt(2/pi) (v +
+// 0.044715 v^3).  Since 0.5 (1 + tanh(u)) = 1 / (1 + e^(-2u)), it is
+// computed as v / (1 + 2^(-2u log2 e)) with the hardware's exp2 and
+// reciprocal (about 1 ulp each): no cancellation near 0, and -0 or v in the
+// tails.
+__device__ __forceinline__ float gelu_tanh(float v) {
+    const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.8853900817779268f * u));
+}
+
 // float32 -> bf16 bits, round to nearest even: gfx950's conversion
 // instruction (v_cvt_pk_bf16_f32) under the default rounding mode.
 __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {

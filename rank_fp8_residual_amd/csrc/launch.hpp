@@ -19,6 +19,7 @@ struct TiledProblem {
     int t_splits;        // K slices per T block (tiled_t_splits())
     unsigned t_target;   // row-tile counter value that marks this launch's T done
     bool out_f32;
+    bool gelu;           // GELU (tanh approximation) on y before its rounding, both outputs
     // fp8-activation mode (both set, or both null): e4m3fn codes of x [M, K]
     // and the rows' scales 2^e [M] from launch_quant_rows; the residual
     // product reads these, T still reads x.
@@ -112,6 +113,7 @@ struct SkinnyProblem {
     float scale;
     int64_t M, K, N, r, r_pad;
     bool out_f32;
+    bool gelu;           // GELU (tanh approximation) on y before its rounding
     SkinnyPlan plan;
 };
 

@@ -55,12 +55,15 @@ struct SArgs {
     int M, K, N, r, r_pad, lda, splits, tiles_n, t_splits;
     int pps;             // T pieces per K slice (16 ranks x a part of the slice each)
     int pwg;             // work-groups of a slice that compute pieces (lowest ids)
-    bool y_vec, out_f32;
+    bool y_vec, out_f32, gelu;
 };
 
 // ------------------------------------------------------------ output tiles
 
-__device__ __forceinline__ void store_out(const SArgs &a, int m, int n, const float (&o)[4]) {
+__device__ __forceinline__ void store_out(const SArgs &a, int m, int n, const float (&y)[4]) {
+    float o[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) o[v] = a.gelu ? gelu_tanh(y[v]) : y[v];
     if (a.out_f32) {
         float *dst = reinterpret_cast<float *>(a.y) + (int64_t)m * a.N + n;
         if (a.y_vec && n + 3 < a.N) {
@@ -606,6 +609,7 @@ hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t 
     a.t_target = p.t_target;
     a.y_vec = (p.N % 4 == 0) && ((uintptr_t)p.y % 16 == 0) && ((uintptr_t)p.partials % 16 == 0);
     a.out_f32 = p.out_f32;
+    a.gelu = p.gelu;
     switch (pl.mb) {
         case 1: return launch_sk_steps<1>(pl.k_slice, a, s);
         case 2: return launch_sk_steps<2>(pl.k_slice, a, s);

@@ -37,6 +37,7 @@ class Option(enum.IntEnum):
     PROFILE = 4
     T_SPLITS = 5
     ACT_FP8 = 6
+    ACTIVATION = 7  # 1 = GELU (tanh approximation) on y, fused into the epilogue
 
 
 class Path(enum.IntEnum):
