@@ -146,6 +146,25 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h,
                                        int64_t r, hipStream_t stream);
 
 /*
+ * litelinear_forward() on activations whose rows are `ldx` elements apart:
+ * x is a row slice of a wider bf16 tensor (for example one part of a fused
+ * projection's output, or every other token of a sequence), read in place
+ * with no copy.  ldx = in is litelinear_forward().
+ *
+ *   x     bf16, row m at x + m * ldx elements, `in` of them used; 16-byte
+ *         aligned, ldx >= in and ldx % 8 == 0 (every row 16-byte aligned).
+ *   the other arguments as in litelinear_forward(); y does not overlap
+ *   x's extent, (M - 1) * ldx + in elements.
+ * Errors: INVALID_ARG (ldx < in), UNSUPPORTED (ldx % 8 != 0), and those of
+ * litelinear_forward().
+ */
+litelinear_status_t litelinear_forward_strided(litelinear_handle_t h,
+                                               const void *x, int64_t ldx, const void *A,
+                                               const void *B, const void *Q, float scale,
+                                               const void *bias, void *y, int64_t M, int64_t in,
+                                               int64_t out, int64_t r, hipStream_t stream);
+
+/*
  * Activations to e4m3fn with one power-of-two scale per row, queued on
  * `stream` (the first step of LITELINEAR_OPT_ACT_FP8, also usable alone).
  *

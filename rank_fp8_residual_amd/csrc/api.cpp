@@ -152,11 +152,15 @@ const char *litelinear_status_string(litelinear_status_t s) {
     return "unknown status";
 }
 
-litelinear_status_t litelinear_check_args(const void *x, const void *A, const void *B, const void *Q,
-                                          const void *bias, const void *y, int64_t M, int64_t in,
-                                          int64_t out, int64_t r, int y_bytes_per_elem) {
+namespace {
+
+// litelinear_check_args() for x rows ldx elements apart.
+litelinear_status_t check_args_ld(const void *x, int64_t ldx, const void *A, const void *B, const void *Q,
+                                  const void *bias, const void *y, int64_t M, int64_t in, int64_t out, int64_t r,
+                                  int y_bytes_per_elem) {
     const int64_t lim = (int64_t)1 << 40;
     if (M < 0 || in < 0 || out < 0 || r < 0) return LITELINEAR_ERR_INVALID_ARG;
+    if (ldx < in || ldx > lim || (double)M * (double)ldx > 4.0e18) return LITELINEAR_ERR_INVALID_ARG;
     if (y_bytes_per_elem != 2 && y_bytes_per_elem != 4) return LITELINEAR_ERR_INVALID_ARG;
     if (M > lim || in > lim || out > lim || r > lim) return LITELINEAR_ERR_INVALID_ARG;
     if ((double)M * (double)in > 4.0e18 || (double)M * (double)out > 1.0e18 ||
@@ -167,17 +171,27 @@ litelinear_status_t litelinear_check_args(const void *x, const void *A, const vo
     if (in > 0 && (!x || !Q)) return LITELINEAR_ERR_INVALID_ARG;
     if (r > 0 && (!A || (in > 0 && !B))) return LITELINEAR_ERR_INVALID_ARG;
     if (in % 16 != 0) return LITELINEAR_ERR_UNSUPPORTED;
-    if (in > 0 && (!aligned(x, 16) || !aligned(Q, 16))) return LITELINEAR_ERR_UNSUPPORTED;
+    if (in > 0 && (!aligned(x, 16) || !aligned(Q, 16) || ldx % 8 != 0)) return LITELINEAR_ERR_UNSUPPORTED;
     if (r > 0 && in > 0 && !aligned(B, 16)) return LITELINEAR_ERR_UNSUPPORTED;
     if (r > 0 && !aligned(A, 2)) return LITELINEAR_ERR_UNSUPPORTED;
     if (bias && !aligned(bias, 2)) return LITELINEAR_ERR_UNSUPPORTED;
     if (!aligned(y, (uintptr_t)y_bytes_per_elem)) return LITELINEAR_ERR_UNSUPPORTED;
     const uint64_t ny = (uint64_t)M * (uint64_t)out * (uint64_t)y_bytes_per_elem;
-    if (overlaps(y, ny, x, (uint64_t)M * in * 2) || overlaps(y, ny, Q, (uint64_t)out * in) ||
+    // x's extent: M - 1 row strides and one row
+    const uint64_t nx = in > 0 ? ((uint64_t)(M - 1) * (uint64_t)ldx + (uint64_t)in) * 2 : 0;
+    if (overlaps(y, ny, x, nx) || overlaps(y, ny, Q, (uint64_t)out * in) ||
         (r > 0 && (overlaps(y, ny, A, (uint64_t)out * r * 2) || overlaps(y, ny, B, (uint64_t)r * in * 2))) ||
         overlaps(y, ny, bias, (uint64_t)out * 2))
         return LITELINEAR_ERR_INVALID_ARG;
     return LITELINEAR_OK;
+}
+
+}  // namespace
+
+litelinear_status_t litelinear_check_args(const void *x, const void *A, const void *B, const void *Q,
+                                          const void *bias, const void *y, int64_t M, int64_t in,
+                                          int64_t out, int64_t r, int y_bytes_per_elem) {
+    return check_args_ld(x, in, A, B, Q, bias, y, M, in, out, r, y_bytes_per_elem);
 }
 
 litelinear_status_t litelinear_create(litelinear_handle_t *out, int device_ordinal) {
@@ -297,7 +311,8 @@ struct OutSet {
 
 // The forward for one output, or for two sharing x and B (s2 != nullptr:
 // the tiled kernel, T computed once).  Arguments are already checked.
-litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, const void *B, const OutSet &s1, const OutSet *s2,
+litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, const void *B, const OutSet &s1,
+                                 const OutSet *s2,
                                  int64_t M, int64_t in, int64_t r, hipStream_t stream) {
     const void *A = s1.A, *Q = s1.Q, *bias = s1.bias;
     void *y = s1.y;
@@ -313,7 +328,7 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, const void *B
     int64_t path = h->opt_path;
     ll::SkinnyPlan plan{};
     const bool skinny_ok = !act8 && in > 0 && ll::skinny_supports(M) &&
-                           ll::skinny_shape_ok(M, in, out, r_pad, plan = ll::skinny_plan(M, in, out, r_pad, h->opt_split));
+                           ll::skinny_shape_ok(M, in, out, r_pad, plan = ll::skinny_plan(M, in, out, r_pad, h->opt_split), ldx);
     if (s2) path = 2;
     if (path == 0) path = (M <= kSkinnyAutoMaxM && skinny_ok && !ll::tiled_tiny_shape(M, in, out, r)) ? 1 : 2;
     if (path == 1 && !skinny_ok) return LITELINEAR_ERR_UNSUPPORTED;
@@ -343,6 +358,7 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, const void *B
         ll::SkinnyProblem p{};
         p.plan = plan;
         p.x = x;
+        p.ldx = ldx;
         p.A = A;
         p.B = B;
         p.Q = Q;
@@ -392,6 +408,7 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, const void *B
 
     ll::TiledProblem p{};
     p.x = x;
+    p.ldx = ldx;
     p.A = A;
     p.B = B;
     p.Q = Q;
@@ -421,7 +438,7 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, const void *B
         st = grow((void **)&h->xs, &h->xs_bytes, (size_t)M * sizeof(float), false);
         if (st != LITELINEAR_OK) return st;
         st = timed_launch(h, LITELINEAR_KERNEL_QUANT, stream,
-                          [&] { return ll::launch_quant_rows(x, h->xq, h->xs, M, in, stream); });
+                          [&] { return ll::launch_quant_rows(x, ldx, h->xq, h->xs, M, in, stream); });
         if (st != LITELINEAR_OK) return st;
         p.xq = h->xq;
         p.xs = h->xs;
@@ -469,17 +486,23 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, const void *B
 
 extern "C" {
 
-litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, const void *A, const void *B,
-                                       const void *Q, float scale, const void *bias, void *y, int64_t M,
-                                       int64_t in, int64_t out, int64_t r, hipStream_t stream) {
+litelinear_status_t litelinear_forward_strided(litelinear_handle_t h, const void *x, int64_t ldx, const void *A,
+                                               const void *B, const void *Q, float scale, const void *bias, void *y,
+                                               int64_t M, int64_t in, int64_t out, int64_t r, hipStream_t stream) {
     if (!h) return LITELINEAR_ERR_INVALID_ARG;
     const bool out_f32 = h->opt_out_f32 != 0;
-    litelinear_status_t st = litelinear_check_args(x, A, B, Q, bias, y, M, in, out, r, out_f32 ? 4 : 2);
+    litelinear_status_t st = check_args_ld(x, ldx, A, B, Q, bias, y, M, in, out, r, out_f32 ? 4 : 2);
     if (st != LITELINEAR_OK) return st;
     if (M == 0 || out == 0) return LITELINEAR_OK;
     DeviceGuard guard(h->device);
     if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
-    return forward_impl(h, x, B, OutSet{A, Q, bias, scale, y, out}, nullptr, M, in, r, stream);
+    return forward_impl(h, x, ldx, B, OutSet{A, Q, bias, scale, y, out}, nullptr, M, in, r, stream);
+}
+
+litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, const void *A, const void *B,
+                                       const void *Q, float scale, const void *bias, void *y, int64_t M,
+                                       int64_t in, int64_t out, int64_t r, hipStream_t stream) {
+    return litelinear_forward_strided(h, x, in, A, B, Q, scale, bias, y, M, in, out, r, stream);
 }
 
 litelinear_status_t litelinear_forward_pair(litelinear_handle_t h, const void *x, const void *B, const void *A1,
@@ -507,11 +530,11 @@ litelinear_status_t litelinear_forward_pair(litelinear_handle_t h, const void *x
     // the time): one forward per output.  Otherwise one tiled launch.
     const bool skinny = h->opt_path == 1 || (h->opt_path == 0 && M <= kSkinnyAutoMaxM && h->opt_act_fp8 == 0);
     if (out1 == 0 || out2 == 0 || in == 0 || skinny) {
-        if (out1 > 0 && (st = forward_impl(h, x, B, s1, nullptr, M, in, r, stream)) != LITELINEAR_OK) return st;
-        if (out2 > 0) st = forward_impl(h, x, B, s2, nullptr, M, in, r, stream);
+        if (out1 > 0 && (st = forward_impl(h, x, in, B, s1, nullptr, M, in, r, stream)) != LITELINEAR_OK) return st;
+        if (out2 > 0) st = forward_impl(h, x, in, B, s2, nullptr, M, in, r, stream);
         return st;
     }
-    return forward_impl(h, x, B, s1, &s2, M, in, r, stream);
+    return forward_impl(h, x, in, B, s1, &s2, M, in, r, stream);
 }
 
 litelinear_status_t litelinear_quantize_rows(litelinear_handle_t h, const void *x, int64_t M, int64_t in,
@@ -529,7 +552,7 @@ litelinear_status_t litelinear_quantize_rows(litelinear_handle_t h, const void *
     DeviceGuard guard(h->device);
     if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
     return timed_launch(h, LITELINEAR_KERNEL_QUANT, stream,
-                        [&] { return ll::launch_quant_rows(x, codes, scales, M, in, stream); });
+                        [&] { return ll::launch_quant_rows(x, in, codes, scales, M, in, stream); });
 }
 
 litelinear_status_t litelinear_quantize_tensor(litelinear_handle_t h, const float *R, int64_t n, void *codes,

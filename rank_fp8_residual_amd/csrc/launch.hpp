@@ -16,6 +16,7 @@ struct TiledProblem {
     float *t_part;       // float32 [t_splits, M, r_pad] partial sums of T (t_splits > 1)
     float scale;
     int64_t M, K, N, r, r_pad;
+    int64_t ldx;         // elements between rows of x (>= K, multiple of 8)
     int t_splits;        // K slices per T block (tiled_t_splits())
     unsigned t_target;   // row-tile counter value that marks this launch's T done
     bool out_f32;
@@ -34,9 +35,10 @@ struct TiledProblem {
     int64_t N2;
 };
 
-// x bf16 [M, K] (K % 8 == 0) -> e4m3fn codes [M, K] and one power-of-two
-// scale per row [M] (see quant.hip).
-hipError_t launch_quant_rows(const void *x, void *codes, float *scales, int64_t M, int64_t K, hipStream_t s);
+// x bf16 [M, K] with rows ldx elements apart (K % 8 == 0, ldx % 8 == 0) ->
+// e4m3fn codes [M, K] and one power-of-two scale per row [M] (see quant.hip).
+hipError_t launch_quant_rows(const void *x, int64_t ldx, void *codes, float *scales, int64_t M, int64_t K,
+                             hipStream_t s);
 
 // Decomposition side (convert.hip).  amax_bits: one device word of
 // workspace, cleared on the stream by each call.
@@ -112,6 +114,7 @@ struct SkinnyProblem {
     float *t_part;       // T pieces, float32 [t_splits, M, r_pad] (r > 0)
     float scale;
     int64_t M, K, N, r, r_pad;
+    int64_t ldx;         // elements between rows of x (>= K, multiple of 8)
     bool out_f32;
     bool gelu;           // GELU (tanh approximation) on y before its rounding
     SkinnyPlan plan;
@@ -121,7 +124,8 @@ bool skinny_supports(int64_t M);  // row counts the skinny kernel takes
 // splits_hint > 0 asks for about that many K slices.
 SkinnyPlan skinny_plan(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t splits_hint);
 int64_t skinny_sync_words(const SkinnyPlan &pl);
-bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, const SkinnyPlan &pl);
+// ldx: elements between rows of x.
+bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, const SkinnyPlan &pl, int64_t ldx);
 // a_eff: A itself, or its zero-padded [N, r_pad] copy (see a_needs_padding).
 hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t s);
 

@@ -52,11 +52,12 @@ __device__ __forceinline__ u32x2 codes8(u32x4 v, float scale, bool bad) {
 template <int NCH>
 __global__ void __launch_bounds__(QWAVES * 64) quant_rows_kernel(const unsigned short *__restrict__ x,
                                                                 unsigned char *__restrict__ codes,
-                                                                float *__restrict__ scales, int M, int K) {
+                                                                float *__restrict__ scales, int M, int K,
+                                                                int64_t ldx) {
     const int lane = threadIdx.x & 63;
     const int m = blockIdx.x * QWAVES + (threadIdx.x >> 6);
     if (m >= M) return;
-    const rsrc_t rx = make_rsrc(x + (int64_t)m * K, (int64_t)K * 2);
+    const rsrc_t rx = make_rsrc(x + (int64_t)m * ldx, (int64_t)K * 2);
     // Pass 1: max |x| as bit patterns (|bf16| orders like its bits) and a
     // flag for exponent field 0xFF (infinity or NaN); past K reads zero.
     unsigned amax = 0, bad = 0;
@@ -120,14 +121,16 @@ __global__ void __launch_bounds__(QWAVES * 64) quant_rows_kernel(const unsigned 
 
 }  // namespace
 
-hipError_t launch_quant_rows(const void *x, void *codes, float *scales, int64_t M, int64_t K, hipStream_t s) {
+hipError_t launch_quant_rows(const void *x, int64_t ldx, void *codes, float *scales, int64_t M, int64_t K,
+                             hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    if (K % 8 != 0 || K * 2 >= ((int64_t)1 << 31) || M >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    if (K % 8 != 0 || ldx % 8 != 0 || ldx < K || K * 2 >= ((int64_t)1 << 31) || M >= ((int64_t)1 << 31))
+        return hipErrorInvalidValue;
     const int grid = (int)((M + QWAVES - 1) / QWAVES);
     const int nch = (int)((K + 511) / 512);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3(grid), dim3(QWAVES * 64), 0, s, (const unsigned short *)x,
-                           (unsigned char *)codes, scales, (int)M, (int)K);
+                           (unsigned char *)codes, scales, (int)M, (int)K, ldx);
     };
     if (nch <= 1)
         go(quant_rows_kernel<1>);

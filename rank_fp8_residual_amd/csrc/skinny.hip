@@ -53,6 +53,7 @@ struct SArgs {
     float *tpart;        // T pieces, float32 [t_splits, r_pad / 16, M, 16]
     float scale;
     int M, K, N, r, r_pad, lda, splits, tiles_n, t_splits;
+    int ldx;             // elements between rows of x (>= K)
     int pps;             // T pieces per K slice (16 ranks x a part of the slice each)
     int pwg;             // work-groups of a slice that compute pieces (lowest ids)
     bool y_vec, out_f32, gelu;
@@ -127,7 +128,7 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
 
     // Uniform descriptors (built here so they stay in scalar registers).
     const rsrc_t rq = make_rsrc(a.Q + (int64_t)n0 * a.K, (int64_t)rows_n * a.K);
-    const rsrc_t rx = make_rsrc(a.x, (int64_t)a.M * a.K * 2);
+    const rsrc_t rx = make_rsrc(a.x, (int64_t)a.M * a.ldx * 2);
     const rsrc_t rp = make_rsrc(a.partials, a.splits > 1 ? (int64_t)a.splits * a.M * a.N * 4 : 0);
     const rsrc_t rb = make_rsrc(a.bias, a.bias ? (int64_t)a.N * 2 : 0);
 
@@ -166,7 +167,7 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
         for (int i = wave; i < total; i += 4) {
             const int row = i / PER_ROW, j = i - row * PER_ROW;
             const int k = kb + 512 * j + 8 * lane;
-            const unsigned off = ((unsigned)row * (unsigned)a.K + (unsigned)k) * 2u + (k < a.K ? 0u : kOOB);
+            const unsigned off = ((unsigned)row * (unsigned)a.ldx + (unsigned)k) * 2u + (k < a.K ? 0u : kOOB);
             bload16_lds(rx, xs + row * XS + 1024 * j, off);
         }
     }
@@ -571,11 +572,11 @@ SkinnyPlan skinny_plan(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t s
 
 int64_t skinny_sync_words(const SkinnyPlan &pl) { return (int64_t)pl.tiles_n + 1; }
 
-bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, const SkinnyPlan &pl) {
+bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, const SkinnyPlan &pl, int64_t ldx) {
     // Every buffer descriptor must stay below 2^31 bytes.
     const int64_t lim = (int64_t)1 << 31;
     // The piece work-groups must all be resident at once (at most one per CU).
-    return (int64_t)SBN * K < lim && M * K * 2 < lim && r_pad * K * 2 < lim && (int64_t)SBN * r_pad * 2 < lim &&
+    return (int64_t)SBN * K < lim && M * ldx * 2 < lim && r_pad * K * 2 < lim && (int64_t)SBN * r_pad * 2 < lim &&
            (int64_t)pl.splits * M * N * 4 < lim && (int64_t)pl.t_splits * M * r_pad * 4 < lim && N * 2 < lim &&
            K < lim && (int64_t)pl.tiles_n * pl.splits < lim && pl.producers <= 256;
 }
@@ -585,6 +586,7 @@ hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t 
     if (!p.sync || (pl.splits > 1 && !p.partials) || (p.r > 0 && !p.t_part)) return hipErrorInvalidValue;
     SArgs a{};
     a.x = (const unsigned char *)p.x;
+    a.ldx = (int)p.ldx;
     a.B = (const unsigned char *)p.B;
     a.Q = (const unsigned char *)p.Q;
     a.A = (const unsigned char *)a_eff;

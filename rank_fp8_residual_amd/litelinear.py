@@ -57,7 +57,7 @@ class Kernel(enum.IntEnum):
 EXPORTS = ("litelinear_create", "litelinear_forward", "litelinear_destroy", "litelinear_check_args",
            "litelinear_set_option", "litelinear_kernel_time", "litelinear_status_string",
            "litelinear_version", "litelinear_quantize_rows", "litelinear_quantize_tensor",
-           "litelinear_residual_quantize", "litelinear_forward_pair")
+           "litelinear_residual_quantize", "litelinear_forward_pair", "litelinear_forward_strided")
 
 
 class LiteLinearError(RuntimeError):
@@ -84,6 +84,9 @@ def lib(path: str | None = None) -> ctypes.CDLL:
         L.litelinear_destroy.restype = ctypes.c_int
         L.litelinear_forward.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, i64, i64, i64, i64, vp]
         L.litelinear_forward.restype = ctypes.c_int
+        L.litelinear_forward_strided.argtypes = [vp, vp, i64, vp, vp, vp, ctypes.c_float, vp, vp, i64, i64, i64,
+                                                 i64, vp]
+        L.litelinear_forward_strided.restype = ctypes.c_int
         L.litelinear_check_args.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int]
         L.litelinear_check_args.restype = ctypes.c_int
         L.litelinear_set_option.argtypes = [vp, ctypes.c_int, i64]
@@ -160,17 +163,30 @@ class Handle:
     def forward(self, x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, Q: torch.Tensor,
                 scale: float, bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
                 stream: torch.cuda.Stream | None = None) -> torch.Tensor:
-        """y = (x B^T) A^T + scale * (x dec(Q)^T) + bias on this handle's device."""
+        """y = (x B^T) A^T + scale * (x dec(Q)^T) + bias on this handle's device.
+
+        x may be a row slice of a wider tensor (last dimension contiguous,
+        rows evenly spaced after flattening the leading dimensions, e.g.
+        ``big[:, :in]``): it is then read in place with its row stride."""
         dev = self.device
         if Q.dtype == torch.float8_e4m3fn:
             Q = Q.view(torch.uint8)
         _expect(Q, "Q", torch.uint8, dev, 2)
         out_features, in_features = Q.shape
-        _expect(x, "x", torch.bfloat16, dev, None)
+        _expect(x, "x", torch.bfloat16, dev, None, contiguous=False)
         if x.shape[-1] != in_features:
             raise ValueError(f"x has {x.shape[-1]} features, Q has {in_features}")
         lead = x.shape[:-1]
-        x2 = x if x.dim() == 2 else x.reshape(math.prod(lead), in_features)
+        if x.numel() == 0:  # nothing is read: any strides
+            x2, ldx = x.reshape(math.prod(lead), in_features), in_features
+        else:
+            if in_features > 1 and x.stride(-1) != 1:
+                raise ValueError("x's last dimension must be contiguous")
+            try:
+                x2 = x if x.dim() == 2 else x.view(math.prod(lead), in_features)
+            except RuntimeError:
+                raise ValueError("x's leading dimensions must flatten to rows of one stride") from None
+            ldx = x2.stride(0) if x2.shape[0] > 1 else in_features
         M = x2.shape[0]
         if A is None or B is None:
             if (A is None) != (B is None):
@@ -195,8 +211,14 @@ class Handle:
             if out.numel() != M * out_features:
                 raise ValueError("out has the wrong number of elements")
         s = _stream_ptr(stream, dev)
-        st = lib().litelinear_forward(self._h, _ptr(x2), _ptr(A) if r else None, _ptr(B) if r else None, _ptr(Q),
-                                      float(scale), _ptr(bias), _ptr(out), M, in_features, out_features, r, s)
+        if ldx == in_features:
+            st = lib().litelinear_forward(self._h, _ptr(x2), _ptr(A) if r else None, _ptr(B) if r else None,
+                                          _ptr(Q), float(scale), _ptr(bias), _ptr(out), M, in_features,
+                                          out_features, r, s)
+        else:
+            st = lib().litelinear_forward_strided(self._h, _ptr(x2), ldx, _ptr(A) if r else None,
+                                                  _ptr(B) if r else None, _ptr(Q), float(scale), _ptr(bias),
+                                                  _ptr(out), M, in_features, out_features, r, s)
         if st:
             _check(st, "litelinear_forward")
         return out if out.dim() == 2 and len(lead) == 1 else out.view(*lead, out_features)
@@ -336,7 +358,7 @@ def _stream_ptr(stream, dev: torch.device):
     return torch.cuda.current_stream(dev).cuda_stream
 
 
-def _expect(t, name, dtype, dev, ndim):
+def _expect(t, name, dtype, dev, ndim, contiguous=True):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
@@ -345,7 +367,7 @@ def _expect(t, name, dtype, dev, ndim):
         raise ValueError(f"{name} is on {t.device}, the handle on {dev}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions")
-    if not t.is_contiguous():
+    if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
