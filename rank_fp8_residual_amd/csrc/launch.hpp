@@ -66,7 +66,7 @@ bool tiled_shape_ok(const TiledProblem &p, TileCfg c);
 int tiled_row_tiles(const TiledProblem &p, TileCfg c);
 hipError_t launch_pad_a(const void *A, void *a_pad, int64_t N, int64_t r, int64_t r_pad, hipStream_t s);
 // K slices per block of T: T is computed by tiled_row_tiles() x (blocks per
-// row tile: 2 of 128 rows for 256 x 128 tiles, else 1) x (r_pad /
+// row tile: 2 of 128 rows for 256-row tiles with 64-column T blocks, else 1) x (r_pad /
 // tiled_t_cols()) x t_splits producer work-groups, enough of them to finish
 // early but few enough to leave most CUs to the output tiles.
 // hint > 0 asks for that many slices (capped at the number of K steps).
