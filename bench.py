@@ -63,12 +63,16 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=300)
+    p.add_argument("--ramp-ms", type=float, default=400.0,
+                   help="untimed steps for at least this long before the warm-up and the timed region "
+                        "(the clocks ramp up under load)")
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--copies", type=int, default=0, help="rotating input/output copies (0: auto)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-summary", action="store_true", help="skip the other workloads")
+    p.add_argument("--no-read-probe", action="store_true", help="skip the 64 MiB HBM read-ceiling probe")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 256 MiB device copy (reference kernel for HBM counters)")
     p.add_argument("--path", default="auto", choices=["auto", "skinny", "tiled"])
@@ -164,6 +168,21 @@ class Runner:
     def step(self, i):
         g = self.sets[i % self.copies]
         self.h.forward(g["x"], g["A"], g["B"], g["Q"], g["scale"], g["bias"], out=g["y"])
+
+    def ramp(self, ms):
+        """Untimed steps for at least `ms` milliseconds of wall time, so that
+        the clocks have ramped up under this load before anything is timed."""
+        import torch
+
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n = 0
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(10):
+                self.step(n)
+                n += 1
+            torch.cuda.synchronize()
+        return {"ms": round((time.perf_counter() - t0) * 1e3, 1), "steps": n}
 
     def timed(self, warmup, steps):
         """Warm up, then time exactly `steps` steps: ms per step."""
@@ -272,6 +291,8 @@ def main():
     run = Runner(w, args, dev, args.copies)
     log(f"{run.copies} rotating copies resident ({run.copies * w.bytes / 2**20:.0f} MiB)")
 
+    clock_ramp = run.ramp(args.ramp_ms)
+    log(f"clock ramp: {clock_ramp['steps']} untimed steps in {clock_ramp['ms']} ms")
     ms_step = run.timed(args.warmup, args.steps)
     tflops = w.flops / (ms_step * 1e-3) / 1e12
     gbs = w.bytes / (ms_step * 1e-3) / 1e9
@@ -296,7 +317,8 @@ def main():
             wo = wl.WORKLOADS[name]
             r = Runner(wo, args, dev, act8=act8)
             steps = 20 if wo.flops > 1e12 else 100
-            ms = r.timed(20 if wo.flops > 1e12 else 300, steps)
+            r.ramp(min(args.ramp_ms, 200.0))
+            ms = r.timed(10 if wo.flops > 1e12 else 100, steps)
             k = r.kernel_times(steps)
             ro = roofline(wo, k, ms, act8)
             key = name + ("+act_fp8" if act8 else "")
@@ -323,6 +345,11 @@ def main():
 
     if args.copy_probe:
         copy_probe(dev)
+    probe = None if args.no_read_probe else read_probe(dev)
+    if probe and summary and "skinny" in summary:
+        summary["skinny"]["vs_read_probe"] = round(probe["best"]["us"] / summary["skinny"]["us_per_step"], 4)
+    if probe and w.name == "skinny" and not run.act8:
+        roof["vs_read_probe"] = round(probe["best"]["us"] / (ms_step * 1e3), 4)
 
     line = {
         "metric": "fused LiteLinear TFLOP/s and HBM GB/s vs roofline, M=3630 in=2048 out=8192 r=64"
@@ -350,6 +377,8 @@ def main():
             "step_us": spread,
         },
         "roofline": roof,
+        "clock_ramp": clock_ramp,
+        "hbm_read_probe": probe,
         "cpu_baseline": cpu,
         "device": device_info(dev),
         "workloads": summary,
@@ -473,6 +502,53 @@ def convert_timing(w, dev, steps=20):
     return {"out": out_f, "in": in_f, "r": r, "us_per_call": round(ms * 1e3, 2),
             "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2), "algorithmic_bytes": nbytes}
+
+
+READ_PROBE_BYTES = 64 << 20  # the skinny workload's residual codes (8192 x 8192 bytes)
+
+
+def read_probe(dev, nbytes=READ_PROBE_BYTES, steps=60):
+    """The chip's plain streaming-read rate for `nbytes`, the ceiling of a
+    path that streams that much once: litelinear_read_probe over rotating
+    copies (past the Infinity Cache), timed like a bench step (events around
+    back-to-back launches), for a sweep of launch shapes; the best is the
+    ceiling."""
+    import torch
+
+    from rank_fp8_residual_amd import Handle
+
+    copies = max(2, math.ceil(4 * MALL_BYTES / nbytes))
+    bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(i) for i in range(copies)]
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    h = Handle(dev.index)
+    results = []
+    for wgs in (256, 512, 1024, 2048):
+        for unroll in (4, 8, 16):
+            for nt in (False, True):
+                launch = lambda i: h.read_probe(bufs[i % copies], sink, wgs, unroll, nt)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                i = 0
+                while (time.perf_counter() - t0) < 0.05 or i < 100:
+                    launch(i)
+                    i += 1
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for j in range(steps):
+                    launch(j)
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / steps * 1e3
+                results.append({"work_groups": wgs, "unroll": unroll, "nontemporal": nt, "us": round(us, 2),
+                                "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    best = min(results, key=lambda r: r["us"])
+    del bufs
+    torch.cuda.empty_cache()
+    log(f"read probe ({nbytes >> 20} MiB, {copies} rotating copies): best {best}")
+    return {"bytes": nbytes, "rotating_copies": copies, "best": best,
+            "frac_of_peak": round(best["GB/s"] / PEAK_HBM_GBS, 4),
+            "sweep": sorted(results, key=lambda r: r["us"])[:6]}
 
 
 def copy_probe(dev, reps=5):

@@ -22,6 +22,17 @@
  *   - Nothing throws or aborts across this ABI; every call returns a status.
  *   - A kernel fault shows up as a HIP error at the caller's next
  *     synchronisation, not as a status of the call that queued it.
+ *   - Work-groups of one forward launch hand T = x B^T to each other through
+ *     device counters.  Their waits rely on work-groups being dispatched in
+ *     id order (producers first) and are bounded; a wait that gives up sets
+ *     the handle's error word, and the next forward call on the handle (or
+ *     litelinear_device_status) returns LITELINEAR_ERR_SYNC.
+ *   - Graph capture: every forward entry point may be captured into a HIP
+ *     graph and replayed, once a call of the same or a larger shape has run
+ *     on the handle outside capture (so that its workspace exists).  The
+ *     counters are back at zero after every launch, and a captured call
+ *     queues no allocation, memset or event.  A call under capture that
+ *     would have to grow the workspace returns LITELINEAR_ERR_UNSUPPORTED.
  */
 #ifndef LITELINEAR_H
 #define LITELINEAR_H
@@ -40,7 +51,10 @@ typedef enum {
     LITELINEAR_ERR_INVALID_ARG = 1, /* NULL required pointer, negative size, y overlapping an input */
     LITELINEAR_ERR_UNSUPPORTED = 2, /* in % 16 != 0, or x / Q / B / y not 16-byte aligned */
     LITELINEAR_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
-    LITELINEAR_ERR_OOM = 4          /* workspace allocation failed */
+    LITELINEAR_ERR_OOM = 4,         /* workspace allocation failed */
+    LITELINEAR_ERR_SYNC = 5         /* an earlier launch on this handle gave up waiting for other
+                                       work-groups of the launch: its output is undefined (see
+                                       litelinear_device_status) */
 } litelinear_status_t;
 
 /* Options set per handle with litelinear_set_option(). */
@@ -91,7 +105,12 @@ typedef enum {
      * v the forward's float32 value, before the one rounding to bf16 (or
      * none with LITELINEAR_OPT_OUTPUT_F32).  Both paths, the fp8-activation
      * mode and both outputs of litelinear_forward_pair(). */
-    LITELINEAR_OPT_ACTIVATION = 7
+    LITELINEAR_OPT_ACTIVATION = 7,
+    /* Test hook for the error path.  0 = off (default); n > 0 = every bounded
+     * wait of the following forward launches looks for one count more than
+     * the launch produces and gives up after n polls, so the kernels finish
+     * normally and the error word gets set (the outputs are undefined). */
+    LITELINEAR_OPT_TEST_WAIT_TIMEOUT = 8
 } litelinear_option_t;
 
 /* Kernels whose time litelinear_kernel_time() reports. */
@@ -111,9 +130,12 @@ typedef enum {
  * path, a padded copy of A for ranks that are not a multiple of 8, the
  * split-K partial sums and counters of the skinny path, the e4m3fn codes and
  * row scales of x in the fp8-activation mode); it grows on demand
- * inside litelinear_forward (hipMalloc, after synchronising the device).
- * Calls on one handle must be ordered (one stream at a time): they share the
- * workspace.
+ * inside the forward calls, stream-ordered on the call's stream
+ * (hipMallocAsync / hipFreeAsync: no other stream or device-wide wait).
+ * Calls on one handle must be ordered (one stream at a time, or streams the
+ * caller orders with events): they share the workspace.  The handle also
+ * owns one word of pinned host memory, mapped into the device, in which
+ * kernels report a wait that gave up.
  * Errors: INVALID_ARG (out == NULL or no such device), HIP, OOM.
  */
 litelinear_status_t litelinear_create(litelinear_handle_t *out, int device_ordinal);
@@ -137,7 +159,9 @@ litelinear_status_t litelinear_create(litelinear_handle_t *out, int device_ordin
  * with float32 accumulation; T = x B^T is rounded once to bf16 before the
  * rank-r product; y is rounded once (nearest even) to bf16.
  * The call returns without synchronising; inputs must stay valid until the
- * stream passes it.  Errors: INVALID_ARG, UNSUPPORTED, HIP, OOM.
+ * stream passes it.  Errors: INVALID_ARG, UNSUPPORTED, HIP, OOM, and SYNC
+ * (returned instead of queueing anything when an earlier launch's wait gave
+ * up; the call after it runs normally).
  */
 litelinear_status_t litelinear_forward(litelinear_handle_t h,
                                        const void *x, const void *A, const void *B,
@@ -254,6 +278,25 @@ litelinear_status_t litelinear_set_option(litelinear_handle_t h, int key, int64_
  * Synchronises on the recorded events.  reset != 0 clears the totals. */
 litelinear_status_t litelinear_kernel_time(litelinear_handle_t h, int kernel,
                                            double *total_ms, int64_t *launches, int reset);
+
+/* LITELINEAR_ERR_SYNC if a bounded wait inside a launch on this handle has
+ * given up since the last report (that launch's output is undefined), else
+ * OK.  It reads the handle's error word without synchronising: synchronise
+ * the stream first to cover every queued call.  Reporting clears the word,
+ * and the next forward call first resets the handle's counters on its
+ * stream.  Errors: INVALID_ARG (h == NULL). */
+litelinear_status_t litelinear_device_status(litelinear_handle_t h);
+
+/* Diagnostic, not part of the forward: the HBM read ceiling that the skinny
+ * path (which streams Q once) is measured against.  Reads `bytes` (a
+ * multiple of 16, src 16-byte aligned) of device memory once with
+ * `work_groups` work-groups of 256 threads, each over one contiguous span,
+ * `unroll` (4, 8 or 16) 16-byte loads in flight per lane, non-temporal when
+ * `nontemporal` != 0; XORs one word per work-group into sink[0 ..
+ * work_groups) (so the reads are not optimised away).  Queued on `stream`.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+litelinear_status_t litelinear_read_probe(litelinear_handle_t h, const void *src, int64_t bytes, int work_groups,
+                                          int unroll, int nontemporal, unsigned *sink, hipStream_t stream);
 
 /* Static text for a status code. */
 const char *litelinear_status_string(litelinear_status_t s);

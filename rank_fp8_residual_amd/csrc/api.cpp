@@ -52,58 +52,74 @@ bool aligned(const void *p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
 }  // namespace
 
+// Workspace buffers of one call (device memory beyond the caller's tensors).
+enum WsBuf {
+    WS_APAD = 0,   // zero-padded copy of A [out, r_pad] (ranks not a multiple of 8, misaligned A)
+    WS_APAD2,      // ... of a pair's second A
+    WS_TWS,        // tiled: T' bf16 [M, r_pad]
+    WS_TWS2,       // ... a pair's second T'
+    WS_TPART,      // K-slice partial sums of T, float32 (both paths)
+    WS_PARTIALS,   // skinny: K-slice partial sums of y, float32 [splits, M, out]
+    WS_XQ,         // fp8-activation mode: e4m3fn codes of x [M, in]
+    WS_XS,         // ... and the rows' scales [M]
+    WS_SYNC,       // counters: zero before and after every launch
+    WS_COUNT
+};
+
+struct DevBuf {
+    void *p = nullptr;
+    size_t bytes = 0;
+};
+
 struct litelinear_ctx {
     int device = 0;
-    void *t_ws = nullptr;
-    size_t t_ws_bytes = 0;
-    unsigned *tile_sync = nullptr;  // tiled path: counters (per row tile and per T block)
-    size_t tile_sync_bytes = 0;
-    float *t_part = nullptr;        // K-slice partial sums of T (both paths)
-    size_t t_part_bytes = 0;
-    // Launches since the counters of each path were zeroed (their T-ready
-    // counters only grow, by a fixed step per launch).
-    unsigned tiled_epoch = 0, skinny_epoch = 0;
-    uint64_t tiled_key = 0, skinny_key = 0;  // layout the counters were last used with
-    void *a_pad = nullptr;          // tiled path: zero-padded copy of A
-    size_t a_pad_bytes = 0;
-    void *a_pad2 = nullptr;         // ... and of a pair's second A
-    size_t a_pad2_bytes = 0;
-    void *t_ws2 = nullptr;          // a pair's second T' workspace
-    size_t t_ws2_bytes = 0;
-    float *partials = nullptr;
-    size_t partials_bytes = 0;
-    unsigned *counters = nullptr;
-    size_t n_counters = 0;
-    void *xq = nullptr;             // fp8-activation mode: e4m3fn codes of x
-    size_t xq_bytes = 0;
-    float *xs = nullptr;            // ... and the rows' scales
-    size_t xs_bytes = 0;
-    unsigned *amax = nullptr;       // decomposition side: max |R| as float bits
-    size_t amax_bytes = 0;
-    int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0, opt_t_splits = 0, opt_act_fp8 = 0, opt_gelu = 0;
+    DevBuf ws[WS_COUNT];
+    DevBuf amax;                    // decomposition side: max |R| as float bits
+    // Error word in host memory mapped into the device: kernels set it when
+    // a bounded wait gives up.
+    unsigned *err_host = nullptr;
+    unsigned *err_dev = nullptr;
+    bool sync_dirty = false;        // counters must be cleared before the next launch
+    int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0, opt_t_splits = 0, opt_act_fp8 = 0,
+            opt_gelu = 0, opt_test_wait = 0;
     Prof prof[kNumKernels];
     std::vector<hipEvent_t> event_pool;
 };
 
 namespace {
 
-litelinear_status_t grow(void **p, size_t *have, size_t need, bool zero) {
-    if (*have >= need) return LITELINEAR_OK;
-    if (*p) {
-        if (hipDeviceSynchronize() != hipSuccess) return LITELINEAR_ERR_HIP;
-        (void)hipFree(*p);
-        *p = nullptr;
-        *have = 0;
+// True while `s` is being captured into a graph: no allocation, memset or
+// event timing may be queued then.
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
     }
-    if (hipMalloc(p, need) != hipSuccess) {
-        *p = nullptr;
+    return st != hipStreamCaptureStatusNone;
+}
+
+// Grows a handle buffer to `need` bytes, stream-ordered on `s` (the old
+// buffer is released once the stream's earlier work is done; nothing else on
+// the device is waited for).  zero: the new memory is cleared on `s` before
+// any later work of the stream uses it.
+litelinear_status_t grow(DevBuf &b, size_t need, bool zero, hipStream_t s, bool in_capture) {
+    if (b.bytes >= need) return LITELINEAR_OK;
+    if (in_capture) return LITELINEAR_ERR_UNSUPPORTED;  // the workspace must be grown before capture
+    const size_t bytes = (need + 255) & ~(size_t)255;
+    if (b.p) {
+        if (hipFreeAsync(b.p, s) != hipSuccess) return LITELINEAR_ERR_HIP;
+        b.p = nullptr;
+        b.bytes = 0;
+    }
+    if (hipMallocAsync(&b.p, bytes, s) != hipSuccess) {
+        b.p = nullptr;
         (void)hipGetLastError();
         return LITELINEAR_ERR_OOM;
     }
-    // Zeroed before any kernel of any stream can use it.
-    if (zero && (hipMemset(*p, 0, need) != hipSuccess || hipDeviceSynchronize() != hipSuccess))
+    if (zero && ll::launch_fill_u32((unsigned *)b.p, (int64_t)(bytes / 4), 0u, s) != hipSuccess)
         return LITELINEAR_ERR_HIP;
-    *have = need;
+    b.bytes = bytes;
     return LITELINEAR_OK;
 }
 
@@ -118,21 +134,32 @@ hipEvent_t take_event(litelinear_ctx *h) {
     return e;
 }
 
-// Launches `fn` on `s`, bracketed by an event pair when profiling is on.
+// Launches `fn` on `s`, bracketed by an event pair when profiling is on
+// (and the stream is not being captured).
 template <class F>
-litelinear_status_t timed_launch(litelinear_ctx *h, int kind, hipStream_t s, F fn) {
+litelinear_status_t timed_launch(litelinear_ctx *h, int kind, hipStream_t s, bool in_capture, F fn) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (h->opt_profile) {
+    const bool prof = h->opt_profile && !in_capture;
+    if (prof) {
         e0 = take_event(h);
         e1 = take_event(h);
         if (!e0 || !e1 || hipEventRecord(e0, s) != hipSuccess) return LITELINEAR_ERR_HIP;
     }
     if (fn() != hipSuccess) return LITELINEAR_ERR_HIP;
-    if (h->opt_profile) {
+    if (prof) {
         if (hipEventRecord(e1, s) != hipSuccess) return LITELINEAR_ERR_HIP;
         h->prof[kind].pending.emplace_back(e0, e1);
     }
     return LITELINEAR_OK;
+}
+
+// A kernel reported a bounded wait that gave up: the status is returned
+// once, and the counters are cleared before the next launch.
+bool take_device_error(litelinear_ctx *h) {
+    if (!h->err_host || __atomic_load_n(h->err_host, __ATOMIC_ACQUIRE) == 0) return false;
+    __atomic_store_n(h->err_host, 0u, __ATOMIC_RELEASE);
+    h->sync_dirty = true;
+    return true;
 }
 
 }  // namespace
@@ -148,6 +175,7 @@ const char *litelinear_status_string(litelinear_status_t s) {
         case LITELINEAR_ERR_UNSUPPORTED: return "unsupported shape or alignment";
         case LITELINEAR_ERR_HIP: return "HIP runtime error";
         case LITELINEAR_ERR_OOM: return "out of device memory";
+        case LITELINEAR_ERR_SYNC: return "a kernel's wait for other work-groups of its launch gave up (output undefined)";
     }
     return "unknown status";
 }
@@ -206,6 +234,18 @@ litelinear_status_t litelinear_create(litelinear_handle_t *out, int device_ordin
     litelinear_ctx *h = new (std::nothrow) litelinear_ctx();
     if (!h) return LITELINEAR_ERR_OOM;
     h->device = device_ordinal;
+    DeviceGuard g(h->device);
+    void *dp = nullptr;
+    if (g.err != hipSuccess ||
+        hipHostMalloc((void **)&h->err_host, 64, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess ||
+        hipHostGetDevicePointer(&dp, h->err_host, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        if (h->err_host) (void)hipHostFree(h->err_host);
+        delete h;
+        return LITELINEAR_ERR_HIP;
+    }
+    *h->err_host = 0;
+    h->err_dev = (unsigned *)dp;
     *out = h;
     return LITELINEAR_OK;
 }
@@ -215,18 +255,14 @@ litelinear_status_t litelinear_destroy(litelinear_handle_t h) {
     litelinear_status_t st = LITELINEAR_OK;
     {
         DeviceGuard g(h->device);
+        // The workspace came from stream-ordered allocations: released the
+        // same way once the device is idle.
         if (hipDeviceSynchronize() != hipSuccess) st = LITELINEAR_ERR_HIP;
-        if (h->t_ws) (void)hipFree(h->t_ws);
-        if (h->tile_sync) (void)hipFree(h->tile_sync);
-        if (h->t_part) (void)hipFree(h->t_part);
-        if (h->a_pad) (void)hipFree(h->a_pad);
-        if (h->a_pad2) (void)hipFree(h->a_pad2);
-        if (h->t_ws2) (void)hipFree(h->t_ws2);
-        if (h->partials) (void)hipFree(h->partials);
-        if (h->counters) (void)hipFree(h->counters);
-        if (h->xq) (void)hipFree(h->xq);
-        if (h->xs) (void)hipFree(h->xs);
-        if (h->amax) (void)hipFree(h->amax);
+        for (DevBuf &b : h->ws)
+            if (b.p) (void)hipFreeAsync(b.p, nullptr);
+        if (h->amax.p) (void)hipFreeAsync(h->amax.p, nullptr);
+        if (hipDeviceSynchronize() != hipSuccess) st = LITELINEAR_ERR_HIP;
+        if (h->err_host) (void)hipHostFree(h->err_host);
         for (auto &p : h->prof)
             for (auto &e : p.pending) {
                 (void)hipEventDestroy(e.first);
@@ -269,6 +305,10 @@ litelinear_status_t litelinear_set_option(litelinear_handle_t h, int key, int64_
             if (value != 0 && value != 1) return LITELINEAR_ERR_INVALID_ARG;
             h->opt_gelu = value;
             return LITELINEAR_OK;
+        case LITELINEAR_OPT_TEST_WAIT_TIMEOUT:
+            if (value < 0 || value > (1 << 20)) return LITELINEAR_ERR_INVALID_ARG;
+            h->opt_test_wait = value;
+            return LITELINEAR_OK;
     }
     return LITELINEAR_ERR_INVALID_ARG;
 }
@@ -297,6 +337,11 @@ litelinear_status_t litelinear_kernel_time(litelinear_handle_t h, int kernel, do
     return st;
 }
 
+litelinear_status_t litelinear_device_status(litelinear_handle_t h) {
+    if (!h) return LITELINEAR_ERR_INVALID_ARG;
+    return take_device_error(h) ? LITELINEAR_ERR_SYNC : LITELINEAR_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -309,17 +354,43 @@ struct OutSet {
     int64_t out;
 };
 
+// Polls before a bounded wait gives up (see the kernels): far beyond any
+// real wait, which ends within microseconds.
+constexpr unsigned kWaitLimit = 1u << 26;
+
+// Where one call's workspace comes from: the handle's own buffers, grown on
+// demand.  need[] holds each buffer's size for the call; take() returns the
+// pointers, or a status.
+struct WsRequest {
+    size_t need[WS_COUNT] = {};
+};
+
+litelinear_status_t take_handle_ws(litelinear_ctx *h, const WsRequest &rq, hipStream_t s, bool in_capture,
+                                   void *(&ptr)[WS_COUNT]) {
+    for (int i = 0; i < WS_COUNT; ++i) {
+        ptr[i] = nullptr;
+        if (rq.need[i] == 0) continue;
+        const litelinear_status_t st = grow(h->ws[i], rq.need[i], i == WS_SYNC, s, in_capture);
+        if (st != LITELINEAR_OK) return st;
+        ptr[i] = h->ws[i].p;
+    }
+    return LITELINEAR_OK;
+}
+
 // The forward for one output, or for two sharing x and B (s2 != nullptr:
 // the tiled kernel, T computed once).  Arguments are already checked.
 litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, const void *B, const OutSet &s1,
-                                 const OutSet *s2,
-                                 int64_t M, int64_t in, int64_t r, hipStream_t stream) {
+                                 const OutSet *s2, int64_t M, int64_t in, int64_t r, hipStream_t stream) {
     const void *A = s1.A, *Q = s1.Q, *bias = s1.bias;
     void *y = s1.y;
     const float scale = s1.scale;
     const int64_t out = s1.out;
     const bool out_f32 = h->opt_out_f32 != 0;
     litelinear_status_t st = LITELINEAR_OK;
+    if (take_device_error(h)) return LITELINEAR_ERR_SYNC;
+    const bool in_capture = capturing(stream);
+    const unsigned wait_limit = h->opt_test_wait > 0 ? (unsigned)h->opt_test_wait : kWaitLimit;
+    const unsigned wait_extra = h->opt_test_wait > 0 ? 1u : 0u;
 
     const int64_t r_pad = r > 0 ? cdiv(r, 64) * 64 : 0;
     // The fp8-activation mode runs on the tiled kernel only (with in == 0
@@ -333,30 +404,24 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
     if (path == 0) path = (M <= kSkinnyAutoMaxM && skinny_ok && !ll::tiled_tiny_shape(M, in, out, r)) ? 1 : 2;
     if (path == 1 && !skinny_ok) return LITELINEAR_ERR_UNSUPPORTED;
 
-    // A whose rows are not whole 16-byte chunks is first copied into a
-    // zero-padded [out, r_pad] buffer (both paths read A in 16-byte chunks).
-    const void *a_eff = A;
-    if (ll::a_needs_padding(r, A)) {
-        st = grow(&h->a_pad, &h->a_pad_bytes, (size_t)out * r_pad * 2, false);
-        if (st != LITELINEAR_OK) return st;
-        st = timed_launch(h, LITELINEAR_KERNEL_PAD_A, stream,
-                          [&] { return ll::launch_pad_a(A, h->a_pad, out, r, r_pad, stream); });
-        if (st != LITELINEAR_OK) return st;
-        a_eff = h->a_pad;
-    }
-    const void *a_eff2 = s2 ? s2->A : nullptr;
-    if (s2 && ll::a_needs_padding(r, s2->A)) {
-        st = grow(&h->a_pad2, &h->a_pad2_bytes, (size_t)s2->out * r_pad * 2, false);
-        if (st != LITELINEAR_OK) return st;
-        st = timed_launch(h, LITELINEAR_KERNEL_PAD_A, stream,
-                          [&] { return ll::launch_pad_a(s2->A, h->a_pad2, s2->out, r, r_pad, stream); });
-        if (st != LITELINEAR_OK) return st;
-        a_eff2 = h->a_pad2;
-    }
+    // Workspace of this call.  A whose rows are not whole 16-byte chunks is
+    // first copied into a zero-padded [out, r_pad] buffer (both paths read A
+    // in 16-byte chunks).
+    WsRequest rq;
+    const bool pad1 = ll::a_needs_padding(r, A), pad2 = s2 && ll::a_needs_padding(r, s2->A);
+    if (pad1) rq.need[WS_APAD] = (size_t)out * r_pad * 2;
+    if (pad2) rq.need[WS_APAD2] = (size_t)s2->out * r_pad * 2;
 
+    ll::SkinnyProblem sp{};
+    ll::TiledProblem p{};
+    ll::TileCfg mc{};
+    bool producers = false;
     if (path == 1) {
-        ll::SkinnyProblem p{};
-        p.plan = plan;
+        sp.plan = plan;
+        if (plan.splits > 1) rq.need[WS_PARTIALS] = (size_t)plan.splits * M * out * sizeof(float);
+        if (r > 0) rq.need[WS_TPART] = (size_t)plan.t_splits * M * r_pad * sizeof(float);
+        rq.need[WS_SYNC] = (size_t)ll::skinny_sync_words(plan) * sizeof(unsigned);
+    } else {
         p.x = x;
         p.ldx = ldx;
         p.A = A;
@@ -372,114 +437,100 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
         p.r_pad = r_pad;
         p.out_f32 = out_f32;
         p.gelu = h->opt_gelu != 0;
-        if (p.plan.splits > 1) {
-            st = grow((void **)&h->partials, &h->partials_bytes, (size_t)p.plan.splits * M * out * sizeof(float),
-                      false);
-            if (st != LITELINEAR_OK) return st;
-            p.partials = h->partials;
+        if (s2) {
+            p.Q2 = s2->Q;
+            p.A2 = s2->A;
+            p.bias2 = s2->bias;
+            p.y2 = s2->y;
+            p.scale2 = s2->scale;
+            p.N2 = s2->out;
         }
-        if (r > 0) {
-            st = grow((void **)&h->t_part, &h->t_part_bytes, (size_t)p.plan.t_splits * M * r_pad * sizeof(float),
-                      false);
-            if (st != LITELINEAR_OK) return st;
-            p.t_part = h->t_part;
+        mc = ll::choose_main_tile(p);
+        if (!ll::tiled_shape_ok(p, mc)) return LITELINEAR_ERR_UNSUPPORTED;
+        if (act8) {
+            rq.need[WS_XQ] = (size_t)M * in;
+            rq.need[WS_XS] = (size_t)M * sizeof(float);
         }
-        size_t cbytes = h->n_counters * sizeof(unsigned);
-        const size_t need = (size_t)ll::skinny_sync_words(p.plan) * sizeof(unsigned);
-        if (cbytes < need) h->skinny_epoch = 0;  // counters start again from zero
-        st = grow((void **)&h->counters, &cbytes, need, true);
-        if (st != LITELINEAR_OK) return st;
-        h->n_counters = cbytes / sizeof(unsigned);
-        p.sync = h->counters;
-        // The T flag sits after the column-tile counters: a new layout or
-        // step (with or without T) starts every counter again from zero, so
-        // no word ever holds another layout's flag.
-        const uint64_t key = ((uint64_t)p.plan.tiles_n << 32) | (uint64_t)(r > 0 ? p.plan.pps * p.plan.splits : 0);
-        if (key != h->skinny_key) {
-            if (hipMemsetAsync(h->counters, 0, cbytes, stream) != hipSuccess) return LITELINEAR_ERR_HIP;
-            h->skinny_key = key;
-            h->skinny_epoch = 0;
+        // With producers, T goes through the T' workspace and the row tiles'
+        // ready counters; small problems compute it in each output tile instead.
+        producers = r > 0 && !ll::tiled_self_t(p, mc);
+        if (producers) {
+            rq.need[WS_TWS] = (size_t)M * r_pad * 2;
+            if (s2) rq.need[WS_TWS2] = (size_t)M * r_pad * 2;
+            p.t_splits = ll::tiled_t_splits(p, mc, h->opt_t_splits);
+            if (p.t_splits > 1) rq.need[WS_TPART] = (size_t)p.t_splits * M * r_pad * sizeof(float);
+            rq.need[WS_SYNC] = (size_t)ll::tiled_sync_words(p, mc) * sizeof(unsigned);
         }
-        p.t_target = (h->skinny_epoch + 1u) * (unsigned)(p.plan.pps * p.plan.splits);
-        st = timed_launch(h, LITELINEAR_KERNEL_SKINNY, stream, [&] { return ll::launch_skinny(p, a_eff, stream); });
-        if (st == LITELINEAR_OK && r > 0) ++h->skinny_epoch;
-        return st;
     }
 
-    ll::TiledProblem p{};
-    p.x = x;
-    p.ldx = ldx;
-    p.A = A;
-    p.B = B;
-    p.Q = Q;
-    p.bias = bias;
-    p.y = y;
-    p.scale = scale;
-    p.M = M;
-    p.K = in;
-    p.N = out;
-    p.r = r;
-    p.r_pad = r_pad;
-    p.out_f32 = out_f32;
-    p.gelu = h->opt_gelu != 0;
-    if (s2) {
-        p.Q2 = s2->Q;
-        p.A2 = s2->A;
-        p.bias2 = s2->bias;
-        p.y2 = s2->y;
-        p.scale2 = s2->scale;
-        p.N2 = s2->out;
+    void *ws[WS_COUNT];
+    st = take_handle_ws(h, rq, stream, in_capture, ws);
+    if (st != LITELINEAR_OK) return st;
+    // After a wait that gave up the counters may hold stale counts.
+    if (h->sync_dirty && h->ws[WS_SYNC].p) {
+        if (ll::launch_fill_u32((unsigned *)h->ws[WS_SYNC].p, (int64_t)(h->ws[WS_SYNC].bytes / 4), 0u, stream) !=
+            hipSuccess)
+            return LITELINEAR_ERR_HIP;
+        h->sync_dirty = false;
     }
-    const ll::TileCfg mc = ll::choose_main_tile(p);
-    if (!ll::tiled_shape_ok(p, mc)) return LITELINEAR_ERR_UNSUPPORTED;
+
+    const void *a_eff = A;
+    if (pad1) {
+        st = timed_launch(h, LITELINEAR_KERNEL_PAD_A, stream, in_capture,
+                          [&] { return ll::launch_pad_a(A, ws[WS_APAD], out, r, r_pad, stream); });
+        if (st != LITELINEAR_OK) return st;
+        a_eff = ws[WS_APAD];
+    }
+    const void *a_eff2 = s2 ? s2->A : nullptr;
+    if (pad2) {
+        st = timed_launch(h, LITELINEAR_KERNEL_PAD_A, stream, in_capture,
+                          [&] { return ll::launch_pad_a(s2->A, ws[WS_APAD2], s2->out, r, r_pad, stream); });
+        if (st != LITELINEAR_OK) return st;
+        a_eff2 = ws[WS_APAD2];
+    }
+
+    if (path == 1) {
+        sp.x = x;
+        sp.ldx = ldx;
+        sp.A = A;
+        sp.B = B;
+        sp.Q = Q;
+        sp.bias = bias;
+        sp.y = y;
+        sp.scale = scale;
+        sp.M = M;
+        sp.K = in;
+        sp.N = out;
+        sp.r = r;
+        sp.r_pad = r_pad;
+        sp.out_f32 = out_f32;
+        sp.gelu = h->opt_gelu != 0;
+        sp.partials = (float *)ws[WS_PARTIALS];
+        sp.t_part = (float *)ws[WS_TPART];
+        sp.sync = (unsigned *)ws[WS_SYNC];
+        sp.err = h->err_dev;
+        sp.wait_limit = wait_limit;
+        sp.wait_extra = wait_extra;
+        return timed_launch(h, LITELINEAR_KERNEL_SKINNY, stream, in_capture,
+                            [&] { return ll::launch_skinny(sp, a_eff, stream); });
+    }
+
     if (act8) {
-        st = grow(&h->xq, &h->xq_bytes, (size_t)M * in, false);
+        p.xq = ws[WS_XQ];
+        p.xs = (float *)ws[WS_XS];
+        st = timed_launch(h, LITELINEAR_KERNEL_QUANT, stream, in_capture,
+                          [&] { return ll::launch_quant_rows(x, ldx, ws[WS_XQ], (float *)ws[WS_XS], M, in, stream); });
         if (st != LITELINEAR_OK) return st;
-        st = grow((void **)&h->xs, &h->xs_bytes, (size_t)M * sizeof(float), false);
-        if (st != LITELINEAR_OK) return st;
-        st = timed_launch(h, LITELINEAR_KERNEL_QUANT, stream,
-                          [&] { return ll::launch_quant_rows(x, ldx, h->xq, h->xs, M, in, stream); });
-        if (st != LITELINEAR_OK) return st;
-        p.xq = h->xq;
-        p.xs = h->xs;
     }
-    // With producers, T goes through the T' workspace and the row tiles'
-    // ready counters; small problems compute it in each output tile instead.
-    const bool producers = r > 0 && !ll::tiled_self_t(p, mc);
-    if (producers) {
-        st = grow(&h->t_ws, &h->t_ws_bytes, (size_t)M * r_pad * 2, false);
-        if (st != LITELINEAR_OK) return st;
-        p.t_ws = h->t_ws;
-        if (s2) {
-            st = grow(&h->t_ws2, &h->t_ws2_bytes, (size_t)M * r_pad * 2, false);
-            if (st != LITELINEAR_OK) return st;
-            p.t_ws2 = h->t_ws2;
-        }
-        p.t_splits = ll::tiled_t_splits(p, mc, h->opt_t_splits);
-        if (p.t_splits > 1) {
-            st = grow((void **)&h->t_part, &h->t_part_bytes, (size_t)p.t_splits * M * r_pad * sizeof(float), false);
-            if (st != LITELINEAR_OK) return st;
-            p.t_part = h->t_part;
-        }
-        const size_t need = (size_t)ll::tiled_sync_words(p, mc) * sizeof(unsigned);
-        if (h->tile_sync_bytes < need) h->tiled_epoch = 0;  // counters start again from zero
-        st = grow((void **)&h->tile_sync, &h->tile_sync_bytes, need, true);
-        if (st != LITELINEAR_OK) return st;
-        // The ready counters of every row tile must have grown by the same
-        // step in every launch so far; a different row-tile count or step
-        // starts them again from zero (ordered on the stream).
-        const uint64_t key = ((uint64_t)ll::tiled_row_tiles(p, mc) << 32) | ll::tiled_flag_step(p, mc);
-        if (key != h->tiled_key) {
-            if (hipMemsetAsync(h->tile_sync, 0, h->tile_sync_bytes, stream) != hipSuccess) return LITELINEAR_ERR_HIP;
-            h->tiled_key = key;
-            h->tiled_epoch = 0;
-        }
-        p.t_target = (h->tiled_epoch + 1u) * ll::tiled_flag_step(p, mc);
-    }
-    st = timed_launch(h, LITELINEAR_KERNEL_MAIN, stream,
-                      [&] { return ll::launch_tiled(p, mc, a_eff, a_eff2, h->tile_sync, stream); });
-    if (st == LITELINEAR_OK && producers) ++h->tiled_epoch;
-    return st;
+    p.t_ws = ws[WS_TWS];
+    p.t_ws2 = ws[WS_TWS2];
+    p.t_part = (float *)ws[WS_TPART];
+    p.err = h->err_dev;
+    p.wait_limit = wait_limit;
+    p.wait_extra = wait_extra;
+    unsigned *sync = producers ? (unsigned *)ws[WS_SYNC] : nullptr;
+    return timed_launch(h, LITELINEAR_KERNEL_MAIN, stream, in_capture,
+                        [&] { return ll::launch_tiled(p, mc, a_eff, a_eff2, sync, stream); });
 }
 
 }  // namespace
@@ -551,7 +602,7 @@ litelinear_status_t litelinear_quantize_rows(litelinear_handle_t h, const void *
         return LITELINEAR_ERR_INVALID_ARG;
     DeviceGuard guard(h->device);
     if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
-    return timed_launch(h, LITELINEAR_KERNEL_QUANT, stream,
+    return timed_launch(h, LITELINEAR_KERNEL_QUANT, stream, capturing(stream),
                         [&] { return ll::launch_quant_rows(x, in, codes, scales, M, in, stream); });
 }
 
@@ -567,7 +618,8 @@ litelinear_status_t litelinear_quantize_tensor(litelinear_handle_t h, const floa
         return LITELINEAR_ERR_INVALID_ARG;
     DeviceGuard guard(h->device);
     if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
-    litelinear_status_t st = grow((void **)&h->amax, &h->amax_bytes, 256, false);
+    const bool in_capture = capturing(stream);
+    litelinear_status_t st = grow(h->amax, 256, false, stream, in_capture);
     if (st != LITELINEAR_OK) return st;
     if (n == 0) {
         const float one = 1.0f;  // scale of an empty (all-zero) tensor
@@ -576,8 +628,9 @@ litelinear_status_t litelinear_quantize_tensor(litelinear_handle_t h, const floa
                    ? LITELINEAR_OK
                    : LITELINEAR_ERR_HIP;
     }
-    return timed_launch(h, LITELINEAR_KERNEL_CONVERT, stream,
-                        [&] { return ll::launch_quant_tensor(R, n, codes, h->amax, scale_out, stream); });
+    return timed_launch(h, LITELINEAR_KERNEL_CONVERT, stream, in_capture, [&] {
+        return ll::launch_quant_tensor(R, n, codes, (unsigned *)h->amax.p, scale_out, stream);
+    });
 }
 
 litelinear_status_t litelinear_residual_quantize(litelinear_handle_t h, const void *W, const void *A, const void *B,
@@ -601,7 +654,8 @@ litelinear_status_t litelinear_residual_quantize(litelinear_handle_t h, const vo
         return LITELINEAR_ERR_INVALID_ARG;
     DeviceGuard guard(h->device);
     if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
-    litelinear_status_t st = grow((void **)&h->amax, &h->amax_bytes, 256, false);
+    const bool in_capture = capturing(stream);
+    litelinear_status_t st = grow(h->amax, 256, false, stream, in_capture);
     if (st != LITELINEAR_OK) return st;
     if (out == 0 || in == 0) {
         const float one = 1.0f;
@@ -610,10 +664,24 @@ litelinear_status_t litelinear_residual_quantize(litelinear_handle_t h, const vo
                    ? LITELINEAR_OK
                    : LITELINEAR_ERR_HIP;
     }
-    return timed_launch(h, LITELINEAR_KERNEL_CONVERT, stream, [&] {
-        return ll::launch_residual_quant(W, r > 0 ? A : nullptr, r > 0 ? B : nullptr, out, in, r, codes, h->amax,
-                                         scale_out, stream);
+    return timed_launch(h, LITELINEAR_KERNEL_CONVERT, stream, in_capture, [&] {
+        return ll::launch_residual_quant(W, r > 0 ? A : nullptr, r > 0 ? B : nullptr, out, in, r, codes,
+                                         (unsigned *)h->amax.p, scale_out, stream);
     });
+}
+
+litelinear_status_t litelinear_read_probe(litelinear_handle_t h, const void *src, int64_t bytes, int work_groups,
+                                         int unroll, int nontemporal, unsigned *sink, hipStream_t stream) {
+    if (!h || !src || !sink || bytes <= 0 || work_groups <= 0 || work_groups > (1 << 20))
+        return LITELINEAR_ERR_INVALID_ARG;
+    if (bytes % 16 != 0 || !aligned(src, 16) || !aligned(sink, 4) || (unroll != 4 && unroll != 8 && unroll != 16))
+        return LITELINEAR_ERR_UNSUPPORTED;
+    if (overlaps(sink, (uint64_t)work_groups * 4, src, (uint64_t)bytes)) return LITELINEAR_ERR_INVALID_ARG;
+    DeviceGuard guard(h->device);
+    if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
+    return ll::launch_read_probe(src, bytes, work_groups, unroll, nontemporal != 0, sink, stream) == hipSuccess
+               ? LITELINEAR_OK
+               : LITELINEAR_ERR_HIP;
 }
 
 }  // extern "C"

@@ -271,7 +271,7 @@ hipError_t launch_quant_tensor(const float *R, int64_t n, void *codes, unsigned 
     if (n * 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const int64_t groups = (n + 3) / 4;
     const int grid = (int)((groups + QT_THREADS - 1) / QT_THREADS < 4096 ? (groups + QT_THREADS - 1) / QT_THREADS : 4096);
-    hipError_t e = hipMemsetAsync(amax_bits, 0, sizeof(unsigned), s);
+    hipError_t e = launch_fill_u32(amax_bits, 1, 0u, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(quant_tensor_kernel<false>, dim3(grid), dim3(QT_THREADS), 0, s, R, n,
                        (unsigned char *)codes, amax_bits, scale_out);
@@ -297,7 +297,7 @@ hipError_t launch_residual_quant(const void *W, const void *A, const void *B, in
     a.r = (int)r;
     const int64_t tiles = ((N + RT - 1) / RT) * ((K + RT - 1) / RT);
     if (tiles >= lim) return hipErrorInvalidValue;
-    hipError_t e = hipMemsetAsync(amax_bits, 0, sizeof(unsigned), s);
+    hipError_t e = launch_fill_u32(amax_bits, 1, 0u, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(residual_kernel<false>, dim3((unsigned)tiles), dim3(R_THREADS), 0, s, a);
     hipLaunchKernelGGL(residual_kernel<true>, dim3((unsigned)tiles), dim3(R_THREADS), 0, s, a);

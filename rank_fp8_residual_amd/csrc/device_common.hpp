@@ -152,6 +152,14 @@ __device__ __forceinline__ unsigned bump_u32(unsigned *p) {
     return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A bounded wait for other work-groups of the launch gave up: set the
+// handle's error word (host memory mapped into the device, written at system
+// scope), which the host turns into a status.  The kernel then carries on,
+// so it still ends normally; its output is undefined.
+__device__ __forceinline__ void report_wait_timeout(unsigned *err) {
+    __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight
 // (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, others left open).
 template <int N>

@@ -18,7 +18,10 @@ struct TiledProblem {
     int64_t M, K, N, r, r_pad;
     int64_t ldx;         // elements between rows of x (>= K, multiple of 8)
     int t_splits;        // K slices per T block (tiled_t_splits())
-    unsigned t_target;   // row-tile counter value that marks this launch's T done
+    unsigned *err;       // host-visible error word (a bounded wait gave up)
+    unsigned wait_limit; // polls before a bounded wait gives up (> 0)
+    unsigned wait_extra; // added to every wait's target: 0, or 1 to make the
+                         // waits give up (a test of the error path)
     bool out_f32;
     bool gelu;           // GELU (tanh approximation) on y before its rounding, both outputs
     // fp8-activation mode (both set, or both null): e4m3fn codes of x [M, K]
@@ -50,6 +53,13 @@ hipError_t launch_quant_tensor(const float *R, int64_t n, void *codes, unsigned 
 hipError_t launch_residual_quant(const void *W, const void *A, const void *B, int64_t N, int64_t K, int64_t r,
                                  void *codes, unsigned *amax_bits, float *scale_out, hipStream_t s);
 
+// HBM read ceiling probe (probe.hip): reads bytes (a multiple of 16) of src
+// once with `wgs` work-groups of 256 threads, `unroll` (4, 8 or 16) 16-byte
+// loads in flight per lane, optionally non-temporal; XORs one word per
+// work-group into sink[0 .. wgs).
+hipError_t launch_read_probe(const void *src, int64_t bytes, int wgs, int unroll, bool nontemporal, unsigned *sink,
+                             hipStream_t s);
+
 // Tile configuration of one launch (work-group tile BM x BN).
 struct TileCfg {
     int bm, bn;
@@ -65,17 +75,18 @@ bool a_needs_padding(int64_t r, const void *A);
 bool tiled_shape_ok(const TiledProblem &p, TileCfg c);
 int tiled_row_tiles(const TiledProblem &p, TileCfg c);
 hipError_t launch_pad_a(const void *A, void *a_pad, int64_t N, int64_t r, int64_t r_pad, hipStream_t s);
+// p[0 .. n) = v, queued on s as a kernel (never a memset node).
+hipError_t launch_fill_u32(unsigned *p, int64_t n, unsigned v, hipStream_t s);
 // K slices per block of T: T is computed by tiled_row_tiles() x (blocks per
 // row tile: 2 of 128 rows for 256-row tiles with 64-column T blocks, else 1) x (r_pad /
 // tiled_t_cols()) x t_splits producer work-groups, enough of them to finish
 // early but few enough to leave most CUs to the output tiles.
 // hint > 0 asks for that many slices (capped at the number of K steps).
 int tiled_t_splits(const TiledProblem &p, TileCfg c, int64_t hint);
-// sync: tiled_sync_words() counters, zero when allocated.  Per row tile, the
-// number of finished T blocks over all launches: it grows by
-// tiled_flag_step() per launch, so launch number e (from 1, counted since the
-// counters were zeroed) sets t_target = e * tiled_flag_step() (mod 2^32).
-// Per T block, finished K slices (left at zero by every launch).
+// sync: tiled_sync_words() counters, zero before the launch and zero again
+// after it: per row tile the T blocks finished (tiled_flag_step() of them
+// complete the row tile's T) and the consumers done reading T' (the last one
+// clears both), per T block the finished K slices (the last slice clears it).
 int64_t tiled_sync_words(const TiledProblem &p, TileCfg c);
 unsigned tiled_flag_step(const TiledProblem &p, TileCfg c);
 // True when the output work-groups compute T themselves (no producers, no
@@ -109,9 +120,11 @@ struct SkinnyProblem {
     const void *x, *A, *B, *Q, *bias;
     void *y;
     float *partials;     // float32 [splits, M, N] (splits > 1)
-    unsigned *sync;      // skinny_sync_words() counters, zero when allocated
-    unsigned t_target;   // launch number e (from 1, since the counters were
-                         // zeroed) times plan.producers, mod 2^32
+    unsigned *sync;      // skinny_sync_words() counters, zero before the
+                         // launch and left at zero by it
+    unsigned *err;       // host-visible error word (a bounded wait gave up)
+    unsigned wait_limit; // polls before a bounded wait gives up (> 0)
+    unsigned wait_extra; // added to the T wait's target (1: a test of the error path)
     float *t_part;       // T pieces, float32 [t_splits, M, r_pad] (r > 0)
     float scale;
     int64_t M, K, N, r, r_pad;

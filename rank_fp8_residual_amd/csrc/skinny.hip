@@ -21,11 +21,15 @@
 //   * That last work-group then waits for T (long since done), adds the
 //     pieces of T in K order, rounds T once to bf16, forms
 //     scale * sum + T A^T + bias and stores y.  The slice counters are left
-//     at zero; the T flag only grows, by the producer count per launch, and
-//     each launch waits for its own target value.
+//     at zero; the T flag counts this launch's pieces, and the last final
+//     work-group to finish reading them (a second counter) sets both back to
+//     zero, so every launch waits for the same constant target and a
+//     captured launch replays correctly.
 // Only final work-groups wait, and only for T pieces.  The piece work-groups
 // have the lowest ids (at most one per CU), so they are dispatched first and
 // compute their pieces before waiting for anything: the waits always end.
+// They are bounded all the same; one that gives up sets the error word that
+// the host reports as a status.
 // Every global load is a buffer load: reads past a descriptor's end return
 // zero, so masking rows, columns and the K tail needs no branch.
 #include "device_common.hpp"
@@ -48,8 +52,11 @@ struct SArgs {
     void *y;
     float *partials;     // [splits, M, N]
     unsigned *cnt;       // [tiles_n] K slices done per column tile
-    unsigned *tflag;     // T pieces finished, counted over all launches
-    unsigned t_target;   // tflag value meaning "this launch's T is complete" (mod 2^32)
+    unsigned *tflag;     // T pieces finished in this launch
+    unsigned *fdone;     // final work-groups done reading the T pieces
+    unsigned *err;       // host-visible error word, set when a bounded wait gives up
+    unsigned t_target;   // tflag value meaning "this launch's T is complete"
+    unsigned wait_limit; // polls before a wait gives up
     float *tpart;        // T pieces, float32 [t_splits, r_pad / 16, M, 16]
     float scale;
     int M, K, N, r, r_pad, lda, splits, tiles_n, t_splits;
@@ -337,7 +344,7 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
     // flag already showed this launch's pieces complete, the T pieces.
     const unsigned tflag0 =
         a.splits > 1 ? tflag_sh : (a.r > 0 ? __builtin_amdgcn_readfirstlane(poll_u32(a.tflag)) : 0u);
-    bool t_ready = a.r <= 0 || (int)(tflag0 - a.t_target) >= 0;
+    bool t_ready = a.r <= 0 || tflag0 >= a.t_target;
 
     constexpr int SB = 4;  // slices per batch of loads
     const unsigned pstride = (unsigned)a.M * (unsigned)a.N * 4u;
@@ -440,10 +447,16 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
         if (!t_ready) {
             // The piece work-groups have the lowest ids and make their pieces
             // before they wait for anything; the bound only guards against a
-            // broken dispatch-order assumption.  Each wave looks for itself.
+            // broken dispatch-order assumption (reported through the error
+            // word).  Each wave looks for itself.
             unsigned spins = 0;
-            while ((int)(__builtin_amdgcn_readfirstlane(poll_u32(a.tflag)) - a.t_target) < 0 && ++spins < (1u << 26))
+            while (__builtin_amdgcn_readfirstlane(poll_u32(a.tflag)) < a.t_target) {
+                if (++spins >= a.wait_limit) {
+                    if (lane == 0) report_wait_timeout(a.err);
+                    break;
+                }
                 __builtin_amdgcn_s_sleep(2);
+            }
             stage_t(0, 0);
         }
         for (int h = 0; h < a.r_pad / 64; ++h) {
@@ -496,6 +509,12 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
                     for (int f = 0; f < WNF; ++f) acc[f][b] = mfma16(af[c][f], tf, acc[f][b]);
                 }
             barrier_lds_sync();  // the next group's staging and bf16 T overwrite these
+        }
+        // Every T piece this work-group reads has landed (the staging waits
+        // above); the launch's last final work-group restarts both counters.
+        if (tid == 0 && bump_u32(a.fdone) == (unsigned)(a.tiles_n - 1)) {
+            __hip_atomic_store(a.tflag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.fdone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
@@ -570,7 +589,7 @@ SkinnyPlan skinny_plan(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t s
     return pl;
 }
 
-int64_t skinny_sync_words(const SkinnyPlan &pl) { return (int64_t)pl.tiles_n + 1; }
+int64_t skinny_sync_words(const SkinnyPlan &pl) { return (int64_t)pl.tiles_n + 2; }
 
 bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, const SkinnyPlan &pl, int64_t ldx) {
     // Every buffer descriptor must stay below 2^31 bytes.
@@ -608,7 +627,11 @@ hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t 
     a.pwg = p.r > 0 ? pl.pwg : 0;
     a.cnt = p.sync;
     a.tflag = p.sync + pl.tiles_n;
-    a.t_target = p.t_target;
+    a.fdone = p.sync + pl.tiles_n + 1;
+    a.t_target = (unsigned)(pl.pps * pl.splits) + p.wait_extra;  // one bump per T piece
+    a.wait_limit = p.wait_limit;
+    a.err = p.err;
+    if (p.r > 0 && (!p.err || p.wait_limit == 0)) return hipErrorInvalidValue;
     a.y_vec = (p.N % 4 == 0) && ((uintptr_t)p.y % 16 == 0) && ((uintptr_t)p.partials % 16 == 0);
     a.out_f32 = p.out_f32;
     a.gelu = p.gelu;

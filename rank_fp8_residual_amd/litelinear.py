@@ -28,6 +28,7 @@ class Status(enum.IntEnum):
     UNSUPPORTED = 2
     HIP = 3
     OOM = 4
+    SYNC = 5  # an earlier launch gave up waiting for other work-groups (see device_status)
 
 
 class Option(enum.IntEnum):
@@ -38,6 +39,7 @@ class Option(enum.IntEnum):
     T_SPLITS = 5
     ACT_FP8 = 6
     ACTIVATION = 7  # 1 = GELU (tanh approximation) on y, fused into the epilogue
+    TEST_WAIT_TIMEOUT = 8  # test hook: n > 0 makes every bounded wait give up after n polls
 
 
 class Path(enum.IntEnum):
@@ -57,7 +59,8 @@ class Kernel(enum.IntEnum):
 EXPORTS = ("litelinear_create", "litelinear_forward", "litelinear_destroy", "litelinear_check_args",
            "litelinear_set_option", "litelinear_kernel_time", "litelinear_status_string",
            "litelinear_version", "litelinear_quantize_rows", "litelinear_quantize_tensor",
-           "litelinear_residual_quantize", "litelinear_forward_pair", "litelinear_forward_strided")
+           "litelinear_residual_quantize", "litelinear_forward_pair", "litelinear_forward_strided",
+           "litelinear_device_status", "litelinear_read_probe")
 
 
 class LiteLinearError(RuntimeError):
@@ -105,6 +108,10 @@ def lib(path: str | None = None) -> ctypes.CDLL:
         L.litelinear_forward_pair.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, i64, vp, vp,
                                               ctypes.c_float, vp, vp, i64, i64, i64, i64, vp]
         L.litelinear_forward_pair.restype = ctypes.c_int
+        L.litelinear_read_probe.argtypes = [vp, vp, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+        L.litelinear_read_probe.restype = ctypes.c_int
+        L.litelinear_device_status.argtypes = [vp]
+        L.litelinear_device_status.restype = ctypes.c_int
         L.litelinear_version.argtypes = []
         L.litelinear_version.restype = ctypes.c_char_p
         if path is None:
@@ -159,6 +166,25 @@ class Handle:
         _check(lib().litelinear_kernel_time(self._h, int(kind), ctypes.byref(ms), ctypes.byref(n), int(reset)),
                "kernel_time")
         return ms.value, n.value
+
+    def device_status(self) -> Status:
+        """SYNC if a bounded wait inside a launch on this handle gave up since
+        the last report (that launch's output is undefined), else OK; reads
+        the error word without synchronising and clears it."""
+        return Status(lib().litelinear_device_status(self._h))
+
+    def read_probe(self, src: torch.Tensor, sink: torch.Tensor, work_groups: int, unroll: int = 8,
+                   nontemporal: bool = False, stream: torch.cuda.Stream | None = None):
+        """Diagnostic: read all of `src` once (the HBM read ceiling; see
+        litelinear_read_probe); `sink` is int32/uint32 with >= work_groups
+        elements."""
+        _expect(src, "src", src.dtype, self.device, None)
+        _expect(sink, "sink", sink.dtype, self.device, None)
+        if sink.element_size() != 4 or sink.numel() < work_groups:
+            raise ValueError("sink must hold work_groups 32-bit words")
+        nbytes = src.numel() * src.element_size()
+        _check(lib().litelinear_read_probe(self._h, src.data_ptr(), nbytes, work_groups, unroll, int(nontemporal),
+                                           sink.data_ptr(), _stream_ptr(stream, self.device)), "litelinear_read_probe")
 
     def forward(self, x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, Q: torch.Tensor,
                 scale: float, bias: torch.Tensor | None = None, out: torch.Tensor | None = None,

@@ -65,3 +65,43 @@ def check(y: np.ndarray, y_ref: np.ndarray, out_f32: bool, rms: float | None = N
     bad = np.abs(y - y_ref) > bound
     assert not bad.any(), {**m, "n_bad": int(bad.sum()), "first_bad": np.argwhere(bad)[:3].tolist()}
     return m
+
+
+def check_full(y_dev: torch.Tensor, ref_rows, M: int, out_f32: bool, chunk: int = 1024) -> dict:
+    """The gates of ``check`` on the whole output of a full-size call.
+
+    ``ref_rows(rows)`` returns the float64 oracle output for an array of row
+    indices; it is called chunk by chunk, the reference is kept whole (the
+    max gate needs RMS over all of it), and the device output is converted
+    to float64 one chunk at a time."""
+    N = y_dev.shape[-1]
+    y_ref = np.empty((M, N), np.float64)
+    for m0 in range(0, M, chunk):
+        y_ref[m0:m0 + chunk] = ref_rows(np.arange(m0, min(M, m0 + chunk), dtype=np.int64))
+    rms = float(np.sqrt(np.mean(np.square(y_ref)))) if y_ref.size else 0.0
+    sum_abs_ref, sum_abs_d, max_d, n_bad, first_bad = 0.0, 0.0, 0.0, 0, None
+    finite = True
+    for m0 in range(0, M, chunk):
+        yr = y_ref[m0:m0 + chunk]
+        y = to_f64(y_dev[m0:m0 + chunk])
+        finite = finite and bool(np.all(np.isfinite(y)))
+        d = np.abs(y - yr)
+        sum_abs_ref += float(np.sum(np.abs(yr)))
+        sum_abs_d += float(np.sum(d))
+        max_d = max(max_d, float(d.max()) if d.size else 0.0)
+        bound = MAX_RMS_GATE * rms
+        if not out_f32:
+            bound = bound + half_ulp_bf16(yr)
+        bad = d > bound
+        if bad.any():
+            n_bad += int(bad.sum())
+            if first_bad is None:
+                i, j = np.argwhere(bad)[0]
+                first_bad = [int(m0 + i), int(j), float(y[i, j]), float(yr[i, j])]
+    m = {"rms": rms, "max_abs": max_d, "max_over_rms": max_d / rms if rms > 0 else 0.0,
+         "rel_l1": sum_abs_d / sum_abs_ref if sum_abs_ref > 0 else sum_abs_d, "finite": finite,
+         "n_bad": n_bad, "first_bad": first_bad, "rows": M}
+    assert finite, m
+    assert m["rel_l1"] <= REL_L1_GATE, m
+    assert n_bad == 0, m
+    return m

@@ -68,7 +68,7 @@ def test_bench_json_line(tmp_path):
         pytest.skip("no GPU")
     print("[case] bench json line (tiny, 5 steps)", file=sys.stderr, flush=True)
     p = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "5",
-                        "--warmup", "5", "--no-summary", "--no-cpu-baseline"],
+                        "--warmup", "5", "--no-summary", "--no-cpu-baseline", "--ramp-ms", "50"],
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert p.returncode == 0, p.stderr[-2000:]
     lines = [ln for ln in p.stdout.splitlines() if ln.strip()]
@@ -86,3 +86,6 @@ def test_bench_json_line(tmp_path):
     assert roof["bound"] in ("hbm", "mfma", "alu") and 0 < roof["frac"] < 1
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert d["device"]["compute_units"] > 0
+    assert d["clock_ramp"]["ms"] >= 50 and d["clock_ramp"]["steps"] > 0
+    probe = d["hbm_read_probe"]
+    assert probe["bytes"] == 64 << 20 and 0 < probe["best"]["GB/s"] < 8000

@@ -118,6 +118,37 @@ def test_exact_inputs_bitwise(dev, shape, out_f32):
         assert bad.size == 0, (path.name, bad[:5].tolist(), y[tuple(bad[0])], expect[tuple(bad[0])])
 
 
+EXACT_GRID_SHAPES = [  # M, in, out, r: the tile sizes and T producers of the full-size workloads
+    (4096, 256, 4096, 64),    # 256 x 256 tiles (ping-pong loop), two 128-row T blocks per row tile
+    (4096, 128, 4096, 256),   # 256 x 256 tiles, 256-column T blocks
+    (3630, 192, 8192, 64),    # the DiT grid: 480 tiles of 256 x 256, a 46-row last row tile
+    (2048, 256, 4096, 64),    # 256 x 128 tiles (lockstep loop), two 128-row T blocks
+    (2000, 320, 4000, 48),    # 256 x 128 tiles with ragged rows, columns and rank
+]
+
+
+@pytest.mark.parametrize("shape", EXACT_GRID_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_exact_inputs_bitwise_large_tiles(dev, shape):
+    """Exact-arithmetic inputs on grids that select the 256 x 256 and
+    256 x 128 tiles: bf16 and float32 outputs equal the oracle bit for bit,
+    on the automatic path and on two calls with different inputs queued back
+    to back on one handle."""
+    M, K, N, r = shape
+    h16, h32 = make_handle(dev, Path.AUTO), make_handle(dev, Path.AUTO, out_f32=True)
+    ds = [wl.exact_inputs(M, K, N, r, seed=s) for s in (M + r, M + r + 1)]
+    gs = [to_dev(d, dev) for d in ds]
+    say("exact large tiles", shape)
+    ys = [(h16.forward(g["x"], g["A"], g["B"], g["Q"], g["scale"], g["bias"]),
+           h32.forward(g["x"], g["A"], g["B"], g["Q"], g["scale"], g["bias"])) for g in gs]
+    torch.cuda.synchronize()
+    for d, (y16, y32) in zip(ds, ys):
+        y_ref = oracle_y(d)
+        for y, expect in ((y32, y_ref), (y16, parity.bf16_of(y_ref))):
+            y = parity.to_f64(y)
+            bad = np.argwhere(y != expect)
+            assert bad.size == 0, (bad[:5].tolist(), y[tuple(bad[0])], expect[tuple(bad[0])])
+
+
 # --------------------------------------------------- random small shapes
 
 RANDOM_SHAPES = [  # M, in, out, r: several tiles and ragged tails
@@ -328,28 +359,8 @@ def sample_rows(M, n=48):
     return rows
 
 
-@pytest.mark.parametrize("name", list(wl.WORKLOADS))
-def test_workload_parity(dev, name):
-    """Full-size workloads in the launch configuration the bench times (the
-    automatic path), checked on rows the oracle computes one by one."""
-    w = wl.WORKLOADS[name]
-    say("workload", name, w)
-    d = wl.make_inputs(w, seed=0)
-    g = to_dev(d, dev)
-    h = make_handle(dev, Path.AUTO)
-    y = run(h, g)
-    assert bool(torch.isfinite(y).all())
-    rows = np.arange(w.M) if w.M <= 64 else sample_rows(w.M)
-    y_ref = oracle_y(d, rows=rows)
-    ys = parity.to_f64(y[torch.from_numpy(rows).to(dev)])
-    m = parity.check(ys, y_ref, False)
-    say("workload", name, {k: round(v, 6) if isinstance(v, float) else v for k, v in m.items()})
-    # the float32-output mode must pass the literal max gate
-    h.set_option(Option.OUTPUT_F32, 1)
-    y32 = run(h, g)
-    parity.check(parity.to_f64(y32[torch.from_numpy(rows).to(dev)]), y_ref, True)
-    del g, y, y32
-    torch.cuda.empty_cache()
+# Full-size workloads are compared over their whole outputs in
+# tests/test_gpu_full.py.
 
 
 # --------------------------------------------------------- edge cases
