@@ -104,13 +104,31 @@ typedef enum {
      *     y = gelu(v) = 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))),
      * v the forward's float32 value, before the one rounding to bf16 (or
      * none with LITELINEAR_OPT_OUTPUT_F32).  Both paths, the fp8-activation
-     * mode and both outputs of litelinear_forward_pair(). */
+     * mode and both outputs of litelinear_forward_pair().
+     * 2 = GEGLU, the gated activation of a projection that a GEGLU module
+     * wraps (the README's *Integration guide* passes such an activation
+     * projection through LiteLinear; Shazeer, "GLU Variants Improve
+     * Transformer", 2020): Q, A and bias hold out = 2F rows, the hidden half
+     * first and then the gate, and
+     *     y [M, F] = v[:, :F] * GELU(v[:, F:]),  GELU(u) = u Phi(u) exactly
+     *     (0.5 u (1 + erf(u / sqrt(2))), the device library's erff),
+     * v the forward's float32 value [M, 2F], rounded once at the end.  out
+     * must be even; y has out / 2 columns.  Both paths and the
+     * fp8-activation mode; litelinear_forward_pair() returns UNSUPPORTED. */
     LITELINEAR_OPT_ACTIVATION = 7,
     /* Test hook for the error path.  0 = off (default); n > 0 = every bounded
      * wait of the following forward launches looks for one count more than
      * the launch produces and gives up after n polls, so the kernels finish
      * normally and the error word gets set (the outputs are undefined). */
-    LITELINEAR_OPT_TEST_WAIT_TIMEOUT = 8
+    LITELINEAR_OPT_TEST_WAIT_TIMEOUT = 8,
+    /* Format of the residual codes Q.  0 = OCP e4m3fn (default: bias 7, max
+     * 448, NaN 0x7F/0xFF); 1 = e4m3fnuz, the format the LiteLinear README's
+     * Features list names for AMD hardware (bias 8, max 240 at 0x7F, no
+     * negative zero, no infinities, 0x80 the only NaN).  Every code is
+     * decoded exactly either way.  e4m3fnuz runs with bf16 activations only
+     * (with LITELINEAR_OPT_ACT_FP8 the forward returns UNSUPPORTED) and on
+     * output tiles of at most 256 x 128. */
+    LITELINEAR_OPT_Q_FORMAT = 9
 } litelinear_option_t;
 
 /* Kernels whose time litelinear_kernel_time() reports. */

@@ -51,6 +51,12 @@ def _bind(lib):
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     lib.oracle_forward_rows.restype = ctypes.c_int
+    lib.oracle_forward_rows_q.argtypes = lib.oracle_forward_rows.argtypes + [ctypes.c_int]
+    lib.oracle_forward_rows_q.restype = ctypes.c_int
+    lib.oracle_e4m3fnuz_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3fnuz_to_f64.restype = ctypes.c_double
+    lib.oracle_decode_e4m3fnuz.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.oracle_decode_e4m3fnuz.restype = None
     lib.oracle_quantize_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                          ctypes.c_void_p]
     lib.oracle_quantize_rows.restype = None
@@ -83,6 +89,15 @@ def decode_e4m3fn(codes, lib=None) -> np.ndarray:
     c = np.ascontiguousarray(np.asarray(codes, dtype=np.int64).astype(np.uint8))
     out = np.empty(c.shape, np.float64)
     lib.oracle_decode_e4m3fn(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def decode_e4m3fnuz(codes, lib=None) -> np.ndarray:
+    """e4m3fnuz codes (any integer array or uint8 tensor) -> float64 values."""
+    lib = lib or library()
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.int64).astype(np.uint8))
+    out = np.empty(c.shape, np.float64)
+    lib.oracle_decode_e4m3fnuz(_ptr(c), c.size, _ptr(out))
     return out
 
 
@@ -146,10 +161,33 @@ def gelu_tanh(v) -> np.ndarray:
     return 0.5 * v * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (v + 0.044715 * v ** 3)))
 
 
+def gelu_erf(v) -> np.ndarray:
+    """The exact GELU in float64 (Hendrycks and Gimpel, "Gaussian Error Linear
+    Units (GELUs)", 2016, section 2): v Phi(v) = 0.5 v (1 + erf(v / sqrt(2))),
+    Phi the standard normal distribution function (erf from scipy)."""
+    from scipy.special import erf
+
+    v = np.asarray(v, dtype=np.float64)
+    return 0.5 * v * (1.0 + erf(v / np.sqrt(2.0)))
+
+
+def geglu(y_pre) -> np.ndarray:
+    """GEGLU of a projection's output (Shazeer, "GLU Variants Improve
+    Transformer", 2020): the 2F columns of y_pre are split into a hidden half
+    [:, :F] and a gate half [:, F:], and the result is hidden * GELU(gate),
+    the exact GELU, in float64 -- the gated feed-forward input that the
+    LiteLinear README's integration guide replaces with a LiteLinear
+    projection (LTX-style models wrap the first linear in a GEGLU)."""
+    y_pre = np.asarray(y_pre, dtype=np.float64)
+    F = y_pre.shape[-1] // 2
+    assert y_pre.shape[-1] == 2 * F, "GEGLU needs an even number of columns"
+    return y_pre[..., :F] * gelu_erf(y_pre[..., F:])
+
+
 def forward(x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,
             Q: torch.Tensor, scale: float, bias: torch.Tensor | None,
             rows=None, threads: int | None = None, want_T: bool = False, lib=None,
-            act_fp8: bool = False):
+            act_fp8: bool = False, q_format: str = "e4m3fn"):
     """float64 forward for all rows of x, or for the row indices in ``rows``.
 
     x bf16 [M, in]; A bf16 [out, r]; B bf16 [r, in]; Q uint8 e4m3fn codes
@@ -157,7 +195,12 @@ def forward(x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,
     float64 [len(rows), out], plus T [len(rows), r] when ``want_T``.
     With ``act_fp8`` the residual product reads x quantised by
     ``quantize_rows`` (the fp8-activation mode); T still reads the bf16 x.
+    ``q_format`` "e4m3fnuz" decodes Q as e4m3fnuz codes (bf16 activations).
     """
+    if q_format not in ("e4m3fn", "e4m3fnuz"):
+        raise ValueError(q_format)
+    if act_fp8 and q_format != "e4m3fn":
+        raise ValueError("the fp8-activation forward takes e4m3fn codes")
     lib = lib or library()
     M, K = x.shape
     N = Q.shape[0]
@@ -175,10 +218,13 @@ def forward(x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,
         nrows = ridx.size
     y = np.empty((nrows, N), np.float64)
     T = np.empty((nrows, max(r, 1)), np.float64) if want_T else None
-    fn = lib.oracle_forward_rows_act8 if act_fp8 else lib.oracle_forward_rows
-    rc = fn(_ptr(xb), _ptr(Ab), _ptr(Bb), _ptr(Qb), ctypes.c_float(scale),
+    args = (_ptr(xb), _ptr(Ab), _ptr(Bb), _ptr(Qb), ctypes.c_float(scale),
             _ptr(bb), M, K, N, r, _ptr(ridx), nrows, _ptr(y), _ptr(T),
             int(threads or default_threads()))
+    if act_fp8:
+        rc = lib.oracle_forward_rows_act8(*args)
+    else:
+        rc = lib.oracle_forward_rows_q(*args, 1 if q_format == "e4m3fnuz" else 0)
     if rc != 0:
         raise ValueError("oracle_forward_rows rejected its arguments")
     if want_T:

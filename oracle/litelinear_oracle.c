@@ -7,7 +7,8 @@
  *
  * What it computes (LiteLinear README, page "moonmath-ai/LiteLinear", the
  * equation in the introduction, with the layouts of the Features list and of
- * SVDLinearLayer on the tt_compressor page, "Forward: y = (x @ B.T) @ A.T"):
+ * SVDLinearLayer on the tt_compressor page, whose forward projects x onto B's
+ * rows first and then applies A, with A [out, r] and B [r, in]):
  *
  *     T[m,k] = sum_j x[m,j] * B[k,j]
  *     y[m,n] = sum_k T[m,k] * A[n,k] + scale * sum_j x[m,j] * dec(Q[n,j]) + bias[n]
@@ -74,29 +75,60 @@ void oracle_decode_e4m3fn(const uint8_t *codes, int64_t n, double *outv)
 }
 
 /*
+ * e4m3fnuz, the residual's format on AMD hardware in the README's Features
+ * list: the same fields, exponent bias 8, no negative zero and no
+ * infinities.  0x80 (the would-be negative zero) is the only NaN;
+ *   e == 0            : (-1)^s * f * 2^-10          (zero and subnormals)
+ *   otherwise         : (-1)^s * (1 + f/8) * 2^(e-8) (largest: 0x7F = 240)
+ */
+double oracle_e4m3fnuz_to_f64(uint8_t b)
+{
+    int s = b >> 7, e = (b >> 3) & 15, f = b & 7;
+    double mag;
+    if (b == 0x80)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)f, -10);
+    else
+#if ORACLE_PLANT == 13
+        mag = ldexp(8.0 + f, e - 10); /* planted: the e4m3fn exponent bias */
+#else
+        mag = ldexp(8.0 + f, e - 11); /* (1 + f/8) * 2^(e-8) */
+#endif
+    return s ? -mag : mag;
+}
+
+void oracle_decode_e4m3fnuz(const uint8_t *codes, int64_t n, double *outv)
+{
+    for (int64_t i = 0; i < n; ++i)
+        outv[i] = oracle_e4m3fnuz_to_f64(codes[i]);
+}
+
+/*
  * Forward for a list of rows of x.
  *   x     bf16 bits [M, in] row-major        A bf16 bits [out, r] row-major
- *   B     bf16 bits [r, in] row-major        Q e4m3fn codes [out, in] row-major
+ *   B     bf16 bits [r, in] row-major        Q 8-bit codes [out, in] row-major
  *   scale float32 dequant multiplier          bias bf16 bits [out] or NULL
  *   rows  nrows row indices into x (NULL: rows 0..nrows-1)
  *   y     double [nrows, out] (output)        T double [nrows, r] or NULL (output)
+ *   q_format  0: Q holds e4m3fn codes; 1: e4m3fnuz codes
  * Returns 0, or -1 on a bad argument or allocation failure.
  */
-int oracle_forward_rows(const uint16_t *x, const uint16_t *A, const uint16_t *B,
-                        const uint8_t *Q, float scale, const uint16_t *bias,
-                        int64_t M, int64_t in, int64_t out, int64_t r,
-                        const int64_t *rows, int64_t nrows, double *y, double *T,
-                        int nthreads)
+int oracle_forward_rows_q(const uint16_t *x, const uint16_t *A, const uint16_t *B,
+                          const uint8_t *Q, float scale, const uint16_t *bias,
+                          int64_t M, int64_t in, int64_t out, int64_t r,
+                          const int64_t *rows, int64_t nrows, double *y, double *T,
+                          int nthreads, int q_format)
 {
     double dec[256];
     double s = (double)scale;
     int bad = 0;
-    if (M < 0 || in < 0 || out < 0 || r < 0 || nrows < 0 || !y)
+    if (M < 0 || in < 0 || out < 0 || r < 0 || nrows < 0 || !y || q_format < 0 || q_format > 1)
         return -1;
     if (nrows > 0 && (!x || (out > 0 && in > 0 && !Q) || (r > 0 && (!A || !B))))
         return -1;
     for (int i = 0; i < 256; ++i)
-        dec[i] = oracle_e4m3fn_to_f64((uint8_t)i);
+        dec[i] = q_format ? oracle_e4m3fnuz_to_f64((uint8_t)i) : oracle_e4m3fn_to_f64((uint8_t)i);
     if (nthreads < 1)
         nthreads = 1;
 
@@ -158,6 +190,16 @@ int oracle_forward_rows(const uint16_t *x, const uint16_t *A, const uint16_t *B,
         free(tr);
     }
     return bad ? -1 : 0;
+}
+
+/* oracle_forward_rows_q for e4m3fn codes. */
+int oracle_forward_rows(const uint16_t *x, const uint16_t *A, const uint16_t *B,
+                        const uint8_t *Q, float scale, const uint16_t *bias,
+                        int64_t M, int64_t in, int64_t out, int64_t r,
+                        const int64_t *rows, int64_t nrows, double *y, double *T,
+                        int nthreads)
+{
+    return oracle_forward_rows_q(x, A, B, Q, scale, bias, M, in, out, r, rows, nrows, y, T, nthreads, 0);
 }
 
 /*

@@ -7,8 +7,8 @@ introduction.)  The work runs in the HIP kernels of ``liblitelinear.so``,
 reached through the C ABI in ``include/litelinear.h``; ``litelinear`` is the
 ctypes binding and ``workloads`` draws the seeded synthetic inputs.
 """
-from .litelinear import (Handle, Kernel, LiteLinearError, Option, Path, Status, check_args,
+from .litelinear import (Activation, Handle, Kernel, LiteLinearError, Option, Path, Status, check_args,
                          default_handle, forward, lib)
 
-__all__ = ["Handle", "Kernel", "LiteLinearError", "Option", "Path", "Status", "check_args",
+__all__ = ["Activation", "Handle", "Kernel", "LiteLinearError", "Option", "Path", "Status", "check_args",
            "default_handle", "forward", "lib"]

@@ -81,7 +81,7 @@ struct litelinear_ctx {
     unsigned *err_dev = nullptr;
     bool sync_dirty = false;        // counters must be cleared before the next launch
     int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0, opt_t_splits = 0, opt_act_fp8 = 0,
-            opt_gelu = 0, opt_test_wait = 0;
+            opt_gelu = 0, opt_test_wait = 0, opt_q_format = 0;
     Prof prof[kNumKernels];
     std::vector<hipEvent_t> event_pool;
 };
@@ -185,7 +185,7 @@ namespace {
 // litelinear_check_args() for x rows ldx elements apart.
 litelinear_status_t check_args_ld(const void *x, int64_t ldx, const void *A, const void *B, const void *Q,
                                   const void *bias, const void *y, int64_t M, int64_t in, int64_t out, int64_t r,
-                                  int y_bytes_per_elem) {
+                                  int y_bytes_per_elem, bool glu = false) {
     const int64_t lim = (int64_t)1 << 40;
     if (M < 0 || in < 0 || out < 0 || r < 0) return LITELINEAR_ERR_INVALID_ARG;
     if (ldx < in || ldx > lim || (double)M * (double)ldx > 4.0e18) return LITELINEAR_ERR_INVALID_ARG;
@@ -204,7 +204,9 @@ litelinear_status_t check_args_ld(const void *x, int64_t ldx, const void *A, con
     if (r > 0 && !aligned(A, 2)) return LITELINEAR_ERR_UNSUPPORTED;
     if (bias && !aligned(bias, 2)) return LITELINEAR_ERR_UNSUPPORTED;
     if (!aligned(y, (uintptr_t)y_bytes_per_elem)) return LITELINEAR_ERR_UNSUPPORTED;
-    const uint64_t ny = (uint64_t)M * (uint64_t)out * (uint64_t)y_bytes_per_elem;
+    // the gated epilogue writes half as many columns as Q has rows
+    if (glu && out % 2 != 0) return LITELINEAR_ERR_INVALID_ARG;
+    const uint64_t ny = (uint64_t)M * (uint64_t)(glu ? out / 2 : out) * (uint64_t)y_bytes_per_elem;
     // x's extent: M - 1 row strides and one row
     const uint64_t nx = in > 0 ? ((uint64_t)(M - 1) * (uint64_t)ldx + (uint64_t)in) * 2 : 0;
     if (overlaps(y, ny, x, nx) || overlaps(y, ny, Q, (uint64_t)out * in) ||
@@ -302,8 +304,12 @@ litelinear_status_t litelinear_set_option(litelinear_handle_t h, int key, int64_
             h->opt_act_fp8 = value;
             return LITELINEAR_OK;
         case LITELINEAR_OPT_ACTIVATION:
-            if (value != 0 && value != 1) return LITELINEAR_ERR_INVALID_ARG;
+            if (value < 0 || value > 2) return LITELINEAR_ERR_INVALID_ARG;
             h->opt_gelu = value;
+            return LITELINEAR_OK;
+        case LITELINEAR_OPT_Q_FORMAT:
+            if (value != 0 && value != 1) return LITELINEAR_ERR_INVALID_ARG;
+            h->opt_q_format = value;
             return LITELINEAR_OK;
         case LITELINEAR_OPT_TEST_WAIT_TIMEOUT:
             if (value < 0 || value > (1 << 20)) return LITELINEAR_ERR_INVALID_ARG;
@@ -394,12 +400,22 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
 
     const int64_t r_pad = r > 0 ? cdiv(r, 64) * 64 : 0;
     // The fp8-activation mode runs on the tiled kernel only (with in == 0
-    // there is no residual product to run in fp8).
+    // there is no residual product to run in fp8), and takes e4m3fn codes.
     const bool act8 = h->opt_act_fp8 != 0 && in > 0;
+    const int q_format = (int)h->opt_q_format;
+    const bool glu = h->opt_gelu == 2;
+    if (act8 && q_format != 0) return LITELINEAR_ERR_UNSUPPORTED;
+    if (glu && (s2 || out % 2 != 0)) return LITELINEAR_ERR_UNSUPPORTED;
     int64_t path = h->opt_path;
     ll::SkinnyPlan plan{};
-    const bool skinny_ok = !act8 && in > 0 && ll::skinny_supports(M) &&
-                           ll::skinny_shape_ok(M, in, out, r_pad, plan = ll::skinny_plan(M, in, out, r_pad, h->opt_split), ldx);
+    // (with the gated epilogue the skinny kernel reads Q, A and the partial
+    // sums through whole-tensor descriptors, each below 2^31 bytes)
+    const int64_t lim31 = (int64_t)1 << 31;
+    const bool skinny_ok =
+        !act8 && in > 0 && ll::skinny_supports(M) &&
+        ll::skinny_shape_ok(M, in, out, r_pad, plan = ll::skinny_plan(M, in, out, r_pad, h->opt_split), ldx) &&
+        (!glu || (out * in < lim31 && out * (r_pad > 0 ? r_pad : 1) * 2 < lim31 &&
+                  (int64_t)plan.splits * M * plan.tiles_n * 128 * 4 < lim31));
     if (s2) path = 2;
     if (path == 0) path = (M <= kSkinnyAutoMaxM && skinny_ok && !ll::tiled_tiny_shape(M, in, out, r)) ? 1 : 2;
     if (path == 1 && !skinny_ok) return LITELINEAR_ERR_UNSUPPORTED;
@@ -418,7 +434,10 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
     bool producers = false;
     if (path == 1) {
         sp.plan = plan;
-        if (plan.splits > 1) rq.need[WS_PARTIALS] = (size_t)plan.splits * M * out * sizeof(float);
+        // partial sums' rows: the products' columns (whole column tiles with
+        // the gated epilogue)
+        const int64_t pcols = glu ? (int64_t)plan.tiles_n * 128 : out;
+        if (plan.splits > 1) rq.need[WS_PARTIALS] = (size_t)plan.splits * M * pcols * sizeof(float);
         if (r > 0) rq.need[WS_TPART] = (size_t)plan.t_splits * M * r_pad * sizeof(float);
         rq.need[WS_SYNC] = (size_t)ll::skinny_sync_words(plan) * sizeof(unsigned);
     } else {
@@ -436,7 +455,10 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
         p.r = r;
         p.r_pad = r_pad;
         p.out_f32 = out_f32;
-        p.gelu = h->opt_gelu != 0;
+        p.gelu = h->opt_gelu == 1;
+        p.glu = glu;
+        p.q_format = q_format;
+        p.act8 = act8;
         if (s2) {
             p.Q2 = s2->Q;
             p.A2 = s2->A;
@@ -504,7 +526,9 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
         sp.r = r;
         sp.r_pad = r_pad;
         sp.out_f32 = out_f32;
-        sp.gelu = h->opt_gelu != 0;
+        sp.gelu = h->opt_gelu == 1;
+        sp.glu = glu;
+        sp.q_format = q_format;
         sp.partials = (float *)ws[WS_PARTIALS];
         sp.t_part = (float *)ws[WS_TPART];
         sp.sync = (unsigned *)ws[WS_SYNC];
@@ -542,7 +566,7 @@ litelinear_status_t litelinear_forward_strided(litelinear_handle_t h, const void
                                                int64_t M, int64_t in, int64_t out, int64_t r, hipStream_t stream) {
     if (!h) return LITELINEAR_ERR_INVALID_ARG;
     const bool out_f32 = h->opt_out_f32 != 0;
-    litelinear_status_t st = check_args_ld(x, ldx, A, B, Q, bias, y, M, in, out, r, out_f32 ? 4 : 2);
+    litelinear_status_t st = check_args_ld(x, ldx, A, B, Q, bias, y, M, in, out, r, out_f32 ? 4 : 2, h->opt_gelu == 2);
     if (st != LITELINEAR_OK) return st;
     if (M == 0 || out == 0) return LITELINEAR_OK;
     DeviceGuard guard(h->device);
@@ -561,6 +585,7 @@ litelinear_status_t litelinear_forward_pair(litelinear_handle_t h, const void *x
                                             const void *A2, const void *Q2, float scale2, const void *bias2, void *y2,
                                             int64_t out2, int64_t M, int64_t in, int64_t r, hipStream_t stream) {
     if (!h) return LITELINEAR_ERR_INVALID_ARG;
+    if (h->opt_gelu == 2) return LITELINEAR_ERR_UNSUPPORTED;  // the gated epilogue has one output
     const int ysz = h->opt_out_f32 != 0 ? 4 : 2;
     litelinear_status_t st = litelinear_check_args(x, A1, B, Q1, bias1, y1, M, in, out1, r, ysz);
     if (st != LITELINEAR_OK) return st;

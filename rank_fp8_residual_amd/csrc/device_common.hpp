@@ -55,6 +55,86 @@ __device__ __forceinline__ void fp8x16_to_bf16x16(u32x4 q, u32x4 &h0, u32x4 &h1)
     h1 = u32x4{c.x, c.y, d.x, d.y};
 }
 
+// e4m3fnuz, the residual's format on AMD hardware (LiteLinear README,
+// Features): exponent bias 8 instead of 7, no negative zero, no infinities.
+// Every code but three decodes to exactly half its e4m3fn value, so the
+// e4m3fn conversion at a multiplier of 0.5 is exact for them.  The three
+// exceptions: 0x7F and 0xFF (e4m3fn NaN, e4m3fnuz +-240) and 0x80 (e4m3fn
+// -0, e4m3fnuz NaN).  A per-tensor quantiser emits +-240 only where it hits
+// the tensor's largest magnitude, so the fix-up below is rare; callers test
+// for it first with fnuz_special_or().
+__device__ __forceinline__ unsigned fnuz_special_or(unsigned acc, unsigned w) {
+    // Byte-wise, with no carry between bytes (t's bytes are at most 0x7F):
+    // t + 0x01 has bit 7 set exactly for the bytes 0x7F and 0xFF, and
+    // ~(t + 0x7F) has bit 7 set exactly for the bytes whose low 7 bits are
+    // zero, of which w's sign bit keeps 0x80.  Only bits 7 of each byte
+    // (mask 0x80808080) of the result mean anything.
+    const unsigned t = w & 0x7F7F7F7Fu;
+    return acc | (t + 0x01010101u) | (~(t + 0x7F7F7F7Fu) & w);
+}
+__device__ __forceinline__ bool fnuz_any_special(unsigned acc) { return (acc & 0x80808080u) != 0u; }
+
+// The three exceptional e4m3fnuz codes of `w`, patched into the bf16 pairs
+// that the halving conversion produced for it: 0x7F -> 240 (bf16 0x4370),
+// 0xFF -> -240 (0xC370), 0x80 -> NaN (0x7FC0).
+__device__ __forceinline__ u32x2 fnuz_patch(unsigned w, u32x2 r) {
+    unsigned v[2] = {r.x, r.y};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const unsigned b = (w >> (8 * i)) & 0xFFu;
+        const unsigned h = b == 0x7Fu ? 0x4370u : (b == 0xFFu ? 0xC370u : 0x7FC0u);
+        const unsigned m = 0xFFFFu << (16 * (i & 1));
+        if (b == 0x7Fu || b == 0xFFu || b == 0x80u) v[i >> 1] = (v[i >> 1] & ~m) | ((h << (16 * (i & 1))) & m);
+    }
+    return u32x2{v[0], v[1]};
+}
+
+// The exceptional e4m3fnuz codes of `w` alone, as bf16 pairs (the layout
+// of the halving conversion's result; every other code gives 0), and `w`
+// with those codes replaced by 0x00 (zero).  The product of the two parts
+// adds up to the product of the exact decode.
+__device__ __forceinline__ u32x2 fnuz_special_values(unsigned w) {
+    unsigned v[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const unsigned b = (w >> (8 * i)) & 0xFFu;
+        const unsigned h = b == 0x7Fu ? 0x4370u : (b == 0xFFu ? 0xC370u : (b == 0x80u ? 0x7FC0u : 0u));
+        v[i >> 1] |= h << (16 * (i & 1));
+    }
+    return u32x2{v[0], v[1]};
+}
+__device__ __forceinline__ unsigned fnuz_without_specials(unsigned w) {
+    unsigned r = w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const unsigned b = (w >> (8 * i)) & 0xFFu;
+        if (b == 0x7Fu || b == 0xFFu || b == 0x80u) r &= ~(0xFFu << (8 * i));
+    }
+    return r;
+}
+
+// Four residual codes -> four bf16 values: QF = 0 e4m3fn, QF = 1 e4m3fnuz
+// (halving conversion; PATCH = true also fixes the three exceptional codes).
+template <int QF, bool PATCH = false>
+__device__ __forceinline__ u32x2 q8x4_to_bf16x4(unsigned w) {
+    if constexpr (QF == 0) {
+        return fp8x4_to_bf16x4(w);
+    } else {
+        const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 0.5f, false);
+        const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 0.5f, true);
+        const u32x2 r{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+        return PATCH ? fnuz_patch(w, r) : r;
+    }
+}
+
+// True on every lane when `p` holds on any lane of the wave.
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// The exact GELU, v Phi(v) = 0.5 v (1 + erf(v / sqrt(2))) (Hendrycks and
+// Gimpel, 2016), with the device library's erff: the gate's activation of
+// the gated epilogue (GEGLU).
+__device__ __forceinline__ float gelu_erf(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
 // GELU in its tanh approximation (Hendrycks and Gimpel, "Gaussian Error
 // Linear Units (GELUs)", 2016): 0.5 v (1 + tanh(u)), u = sqrt(2/pi) (v +
 // 0.044715 v^3).  Since 0.5 (1 + tanh(u)) = 1 / (1 + e^(-2u)), it is

@@ -24,6 +24,10 @@ struct TiledProblem {
                          // waits give up (a test of the error path)
     bool out_f32;
     bool gelu;           // GELU (tanh approximation) on y before its rounding, both outputs
+    int q_format;        // Q codes: 0 e4m3fn, 1 e4m3fnuz (bf16 activations only)
+    bool act8;           // the fp8-activation mode will run (xq, xs set before the launch)
+    bool glu;            // gated epilogue: N = 2F rows of Q/A/bias (hidden then gate),
+                         // y [M, F] = hidden * GELU_erf(gate); one output only
     // fp8-activation mode (both set, or both null): e4m3fn codes of x [M, K]
     // and the rows' scales 2^e [M] from launch_quant_rows; the residual
     // product reads these, T still reads x.
@@ -131,6 +135,8 @@ struct SkinnyProblem {
     int64_t ldx;         // elements between rows of x (>= K, multiple of 8)
     bool out_f32;
     bool gelu;           // GELU (tanh approximation) on y before its rounding
+    int q_format;        // Q codes: 0 e4m3fn, 1 e4m3fnuz
+    bool glu;            // gated epilogue: N = 2F (hidden, then gate), y [M, F]
     SkinnyPlan plan;
 };
 

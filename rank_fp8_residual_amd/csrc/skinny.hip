@@ -64,31 +64,40 @@ struct SArgs {
     int pps;             // T pieces per K slice (16 ranks x a part of the slice each)
     int pwg;             // work-groups of a slice that compute pieces (lowest ids)
     bool y_vec, out_f32, gelu;
+    // Gated epilogue: Q, A and bias hold 2F rows (hidden, then gate), y is
+    // [M, F] = hidden * GELU_erf(gate).  A work-group's 128 columns of the
+    // products are 64 output columns twice: wave w's fragment 0 is hidden
+    // columns [64 tn + 16 w, +16), fragment 1 the gate of the same columns.
+    // N is then the products' column count (tiles_n x 128, the partial
+    // sums' row length) and NO = F the output's; otherwise NO = N.
+    bool glu;
+    int F, NO;
 };
 
 // ------------------------------------------------------------ output tiles
 
+// y[m][n .. n + 3] = y (past NO dropped), through the activation option.
 __device__ __forceinline__ void store_out(const SArgs &a, int m, int n, const float (&y)[4]) {
     float o[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) o[v] = a.gelu ? gelu_tanh(y[v]) : y[v];
     if (a.out_f32) {
-        float *dst = reinterpret_cast<float *>(a.y) + (int64_t)m * a.N + n;
-        if (a.y_vec && n + 3 < a.N) {
+        float *dst = reinterpret_cast<float *>(a.y) + (int64_t)m * a.NO + n;
+        if (a.y_vec && n + 3 < a.NO) {
             *reinterpret_cast<f32x4 *>(dst) = f32x4{o[0], o[1], o[2], o[3]};
         } else {
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                if (n + v < a.N) dst[v] = o[v];
+                if (n + v < a.NO) dst[v] = o[v];
         }
     } else {
-        unsigned short *dst = reinterpret_cast<unsigned short *>(a.y) + (int64_t)m * a.N + n;
-        if (a.y_vec && n + 3 < a.N) {
+        unsigned short *dst = reinterpret_cast<unsigned short *>(a.y) + (int64_t)m * a.NO + n;
+        if (a.y_vec && n + 3 < a.NO) {
             *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         } else {
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                if (n + v < a.N) dst[v] = f32_to_bf16_rne(o[v]);
+                if (n + v < a.NO) dst[v] = f32_to_bf16_rne(o[v]);
         }
     }
 }
@@ -104,7 +113,8 @@ constexpr int t_kwave() {
     return NSTEPS * 16 < 256 ? NSTEPS * 16 : 256;
 }
 
-template <int MB, int NSTEPS>
+// QF: residual codes in e4m3fn (0) or e4m3fnuz (1).
+template <int MB, int NSTEPS, int QF>
 __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
     constexpr int KS = NSTEPS * 64;            // K elements per slice
     constexpr int XS = (KS + XPAD) * 2;        // LDS bytes per row of x
@@ -132,12 +142,22 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
     const int n0 = tn * SBN, nw = n0 + wave * (WNF * 16);
     const int kb = slice * KS;
     const int rows_n = (a.N - n0) < SBN ? (a.N - n0) : SBN;
+    // Gated epilogue: output column of the wave's first lane row, and this
+    // lane's row of Q and A for fragment f (f = 0 hidden, 1 gate).
+    const int c0 = tn * (SBN / 2) + wave * 16;
+    const bool glu_ok = c0 + l16 < a.F;
 
     // Uniform descriptors (built here so they stay in scalar registers).
-    const rsrc_t rq = make_rsrc(a.Q + (int64_t)n0 * a.K, (int64_t)rows_n * a.K);
+    const rsrc_t rq = a.glu ? make_rsrc(a.Q, (int64_t)2 * a.F * a.K) : make_rsrc(a.Q + (int64_t)n0 * a.K, (int64_t)rows_n * a.K);
     const rsrc_t rx = make_rsrc(a.x, (int64_t)a.M * a.ldx * 2);
     const rsrc_t rp = make_rsrc(a.partials, a.splits > 1 ? (int64_t)a.splits * a.M * a.N * 4 : 0);
-    const rsrc_t rb = make_rsrc(a.bias, a.bias ? (int64_t)a.N * 2 : 0);
+    const rsrc_t rb = make_rsrc(a.bias, a.bias ? (int64_t)(a.glu ? 2 * a.F : a.N) * 2 : 0);
+    // row of Q / A (relative to rq / ra) of this lane in fragment f, past
+    // the end when it does not exist
+    auto wrow = [&](int f) -> unsigned {
+        if (a.glu) return glu_ok ? (unsigned)(f * a.F + c0 + l16) : 0x7FFFFFFFu;
+        return (unsigned)(wave * (WNF * 16) + 16 * f + l16);
+    };
 
     // Bias of this lane's columns, requested first (past N and a missing
     // bias read as zero).
@@ -145,21 +165,29 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
 #pragma unroll
     for (int f = 0; f < WNF; ++f)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) bv[f][v] = bload_bf16(rb, (unsigned)(nw + 16 * f + 4 * g + v));
+        for (int v = 0; v < 4; ++v) {
+            if (a.glu) {
+                const int cc = c0 + 4 * g + v;
+                bv[f][v] = bload_bf16(rb, (unsigned)(f * a.F + cc) + (cc < a.F ? 0u : kOOB / 2));
+            } else {
+                bv[f][v] = bload_bf16(rb, (unsigned)(nw + 16 * f + 4 * g + v));
+            }
+        }
 
     // The first 64 ranks of this lane's A rows, also requested up front: A is
     // read from HBM for the first time, and only a final work-group (any
     // work-group may be one) uses it, after its Q stream.
-    const rsrc_t ra = make_rsrc(a.A + (int64_t)n0 * a.lda * 2, (int64_t)rows_n * a.lda * 2);
+    const rsrc_t ra = a.glu ? make_rsrc(a.A, (int64_t)2 * a.F * a.lda * 2)
+                            : make_rsrc(a.A + (int64_t)n0 * a.lda * 2, (int64_t)rows_n * a.lda * 2);
     auto load_a = [&](u32x4 (&af)[2][WNF], int h) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int f = 0; f < WNF; ++f) {
                 const int ka = 64 * h + 32 * c + 8 * g;
-                af[c][f] = bload16(ra, ((unsigned)(wave * (WNF * 16) + 16 * f + l16) * (unsigned)a.lda + (unsigned)ka) *
-                                               2u +
-                                           (ka < a.lda ? 0u : kOOB));
+                const unsigned row = wrow(f);
+                af[c][f] = bload16(ra, (row * (unsigned)a.lda + (unsigned)ka) * 2u +
+                                           (ka < a.lda && row != 0x7FFFFFFFu ? 0u : kOOB));
             }
     };
     u32x4 af0[2][WNF];
@@ -197,13 +225,19 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
     const bool has_piece = piece_wg && a.r > 0;
     if (has_piece) load_b(bfirst, tn);
 
-    // Q: lane holds codes [k + 16 g, +16) of row nw + 16 f + l16.
+    // Q: lane holds codes [k + 16 g, +16) of row nw + 16 f + l16 (of row
+    // wrow(f) with the gated epilogue).
+    unsigned qoff[WNF];
+#pragma unroll
+    for (int f = 0; f < WNF; ++f) {
+        const unsigned row = wrow(f);
+        qoff[f] = row == 0x7FFFFFFFu ? kOOB : row * (unsigned)a.K;
+    }
     auto load_q = [&](u32x4 (&q)[WNF], int s) {
         const int k = kb + 64 * s + 16 * g;
         const unsigned oob = k < a.K ? 0u : kOOB;
 #pragma unroll
-        for (int f = 0; f < WNF; ++f)
-            q[f] = bload16(rq, (unsigned)(wave * (WNF * 16) + 16 * f + l16) * (unsigned)a.K + (unsigned)k + oob);
+        for (int f = 0; f < WNF; ++f) q[f] = bload16(rq, qoff[f] + (unsigned)k + oob);
     };
     u32x4 qr[D][WNF];
 #pragma unroll
@@ -285,7 +319,25 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
 #pragma unroll
         for (int f = 0; f < WNF; ++f) {
             u32x4 h0, h1;
-            fp8x16_to_bf16x16(qr[s % D][f], h0, h1);
+            const u32x4 q = qr[s % D][f];
+            if constexpr (QF == 0) {
+                fp8x16_to_bf16x16(q, h0, h1);
+            } else {
+                // e4m3fnuz: the halving conversion, and the fix-up of the
+                // three exceptional codes in the rare lane that holds one
+                u32x2 c[4] = {q8x4_to_bf16x4<1>(q.x), q8x4_to_bf16x4<1>(q.y), q8x4_to_bf16x4<1>(q.z),
+                              q8x4_to_bf16x4<1>(q.w)};
+                const unsigned sp = fnuz_special_or(fnuz_special_or(fnuz_special_or(fnuz_special_or(0u, q.x), q.y), q.z),
+                                                    q.w);
+                if (fnuz_any_special(sp)) {
+                    c[0] = fnuz_patch(q.x, c[0]);
+                    c[1] = fnuz_patch(q.y, c[1]);
+                    c[2] = fnuz_patch(q.z, c[2]);
+                    c[3] = fnuz_patch(q.w, c[3]);
+                }
+                h0 = u32x4{c[0].x, c[0].y, c[1].x, c[1].y};
+                h1 = u32x4{c[2].x, c[2].y, c[3].x, c[3].y};
+            }
 #pragma unroll
             for (int b = 0; b < MB; ++b) {
                 acc[f][b] = mfma16(h0, x0[b], acc[f][b]);
@@ -518,40 +570,60 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
         }
     }
 
+    if (a.glu) {
+        // y = hidden * GELU_erf(gate): fragment 0 holds the hidden columns
+        // c0 + 4 g .. of this lane, fragment 1 their gate
+        const int n = c0 + 4 * g;
+        if (n < a.F) {
 #pragma unroll
-    for (int f = 0; f < WNF; ++f) {
-        const int n = nw + f * 16 + 4 * g;
-        if (n >= a.N) continue;
+            for (int b = 0; b < MB; ++b) {
+                const int m = b * 16 + l16;
+                if (m >= a.M) continue;
+                float o[4];
 #pragma unroll
-        for (int b = 0; b < MB; ++b) {
-            const int m = b * 16 + l16;
-            if (m >= a.M) continue;
-            const float o[4] = {acc[f][b][0] + bv[f][0], acc[f][b][1] + bv[f][1], acc[f][b][2] + bv[f][2],
-                                acc[f][b][3] + bv[f][3]};
-            store_out(a, m, n, o);
+                for (int v = 0; v < 4; ++v) o[v] = (acc[0][b][v] + bv[0][v]) * gelu_erf(acc[1][b][v] + bv[1][v]);
+                store_out(a, m, n, o);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int f = 0; f < WNF; ++f) {
+            const int n = nw + f * 16 + 4 * g;
+            if (n >= a.N) continue;
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+                const int m = b * 16 + l16;
+                if (m >= a.M) continue;
+                const float o[4] = {acc[f][b][0] + bv[f][0], acc[f][b][1] + bv[f][1], acc[f][b][2] + bv[f][2],
+                                    acc[f][b][3] + bv[f][3]};
+                store_out(a, m, n, o);
+            }
         }
     }
     if (a.splits > 1 && tid == 0) __hip_atomic_store(&a.cnt[tn], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int MB, int NSTEPS>
-hipError_t launch_sk(const SArgs &a, hipStream_t s) {
+hipError_t launch_sk(const SArgs &a, int qf, hipStream_t s) {
     if constexpr (x_lds_bytes<MB, NSTEPS>() + 4 * MB * 64 * 16 + 64 > LDS_MAX) {
         return hipErrorInvalidValue;
     } else {
         const int grid = a.tiles_n * a.splits;
-        hipLaunchKernelGGL((skinny_kernel<MB, NSTEPS>), dim3(grid), dim3(SNT), 0, s, a);
+        if (qf)
+            hipLaunchKernelGGL((skinny_kernel<MB, NSTEPS, 1>), dim3(grid), dim3(SNT), 0, s, a);
+        else
+            hipLaunchKernelGGL((skinny_kernel<MB, NSTEPS, 0>), dim3(grid), dim3(SNT), 0, s, a);
         return hipGetLastError();
     }
 }
 
 template <int MB>
-hipError_t launch_sk_steps(int k_slice, const SArgs &a, hipStream_t s) {
+hipError_t launch_sk_steps(int k_slice, const SArgs &a, int qf, hipStream_t s) {
     switch (k_slice / 64) {
-        case 8: return launch_sk<MB, 8>(a, s);
-        case 16: return launch_sk<MB, 16>(a, s);
-        case 32: return launch_sk<MB, 32>(a, s);
-        case 64: return launch_sk<MB, 64>(a, s);
+        case 8: return launch_sk<MB, 8>(a, qf, s);
+        case 16: return launch_sk<MB, 16>(a, qf, s);
+        case 32: return launch_sk<MB, 32>(a, qf, s);
+        case 64: return launch_sk<MB, 64>(a, qf, s);
     }
     return hipErrorInvalidValue;
 }
@@ -616,7 +688,11 @@ hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t 
     a.scale = p.scale;
     a.M = (int)p.M;
     a.K = (int)p.K;
-    a.N = (int)p.N;
+    if (p.glu && p.N % 2 != 0) return hipErrorInvalidValue;
+    a.glu = p.glu;
+    a.F = p.glu ? (int)(p.N / 2) : 0;
+    a.N = p.glu ? pl.tiles_n * SBN : (int)p.N;  // the products' columns (partial sums' row length)
+    a.NO = p.glu ? a.F : (int)p.N;
     a.r = (int)p.r;
     a.r_pad = (int)p.r_pad;
     a.lda = a_eff == p.A ? (int)p.r : (int)p.r_pad;
@@ -632,13 +708,13 @@ hipError_t launch_skinny(const SkinnyProblem &p, const void *a_eff, hipStream_t 
     a.wait_limit = p.wait_limit;
     a.err = p.err;
     if (p.r > 0 && (!p.err || p.wait_limit == 0)) return hipErrorInvalidValue;
-    a.y_vec = (p.N % 4 == 0) && ((uintptr_t)p.y % 16 == 0) && ((uintptr_t)p.partials % 16 == 0);
+    a.y_vec = (a.NO % 4 == 0) && ((uintptr_t)p.y % 16 == 0) && ((uintptr_t)p.partials % 16 == 0);
     a.out_f32 = p.out_f32;
     a.gelu = p.gelu;
     switch (pl.mb) {
-        case 1: return launch_sk_steps<1>(pl.k_slice, a, s);
-        case 2: return launch_sk_steps<2>(pl.k_slice, a, s);
-        case 4: return launch_sk_steps<4>(pl.k_slice, a, s);
+        case 1: return launch_sk_steps<1>(pl.k_slice, a, p.q_format, s);
+        case 2: return launch_sk_steps<2>(pl.k_slice, a, p.q_format, s);
+        case 4: return launch_sk_steps<4>(pl.k_slice, a, p.q_format, s);
     }
     return hipErrorInvalidValue;
 }

@@ -40,6 +40,13 @@ class Option(enum.IntEnum):
     ACT_FP8 = 6
     ACTIVATION = 7  # 1 = GELU (tanh approximation) on y, fused into the epilogue
     TEST_WAIT_TIMEOUT = 8  # test hook: n > 0 makes every bounded wait give up after n polls
+    Q_FORMAT = 9  # residual codes: 0 e4m3fn, 1 e4m3fnuz
+
+
+class Activation(enum.IntEnum):
+    NONE = 0
+    GELU_TANH = 1  # GELU (tanh approximation) on every element of y
+    GEGLU = 2      # y [M, out/2] = hidden * GELU_erf(gate), halves of the 2F-row projection
 
 
 class Path(enum.IntEnum):
@@ -142,6 +149,7 @@ class Handle:
         self._h = ctypes.c_void_p()
         _check(lib().litelinear_create(ctypes.byref(self._h), self.device.index or 0), "litelinear_create")
         self.out_f32 = False
+        self.activation = Activation.NONE
 
     def close(self):
         if self._h:
@@ -159,6 +167,8 @@ class Handle:
         _check(lib().litelinear_set_option(self._h, int(key), int(value)), f"set_option({key})")
         if int(key) == Option.OUTPUT_F32:
             self.out_f32 = bool(value)
+        if int(key) == Option.ACTIVATION:
+            self.activation = Activation(value)
 
     def kernel_time(self, kind: Kernel | int, reset: bool = False):
         """(total milliseconds, launches) recorded for one kernel kind."""
@@ -195,10 +205,12 @@ class Handle:
         rows evenly spaced after flattening the leading dimensions, e.g.
         ``big[:, :in]``): it is then read in place with its row stride."""
         dev = self.device
-        if Q.dtype == torch.float8_e4m3fn:
+        if Q.dtype in (torch.float8_e4m3fn, torch.float8_e4m3fnuz):
             Q = Q.view(torch.uint8)
         _expect(Q, "Q", torch.uint8, dev, 2)
         out_features, in_features = Q.shape
+        # the gated epilogue's output has half as many columns as Q has rows
+        y_cols = out_features // 2 if self.activation == Activation.GEGLU else out_features
         _expect(x, "x", torch.bfloat16, dev, None, contiguous=False)
         if x.shape[-1] != in_features:
             raise ValueError(f"x has {x.shape[-1]} features, Q has {in_features}")
@@ -231,10 +243,10 @@ class Handle:
                 raise ValueError("bias must have out_features elements")
         ydt = torch.float32 if self.out_f32 else torch.bfloat16
         if out is None:
-            out = torch.empty((M, out_features), dtype=ydt, device=dev)
+            out = torch.empty((M, y_cols), dtype=ydt, device=dev)
         else:
             _expect(out, "out", ydt, dev, None)
-            if out.numel() != M * out_features:
+            if out.numel() != M * y_cols:
                 raise ValueError("out has the wrong number of elements")
         s = _stream_ptr(stream, dev)
         if ldx == in_features:
@@ -247,7 +259,7 @@ class Handle:
                                                   _ptr(out), M, in_features, out_features, r, s)
         if st:
             _check(st, "litelinear_forward")
-        return out if out.dim() == 2 and len(lead) == 1 else out.view(*lead, out_features)
+        return out if out.dim() == 2 and len(lead) == 1 else out.view(*lead, y_cols)
 
     def forward_pair(self, x: torch.Tensor, B: torch.Tensor | None, first: tuple, second: tuple,
                      out: tuple | None = None, stream: torch.cuda.Stream | None = None):

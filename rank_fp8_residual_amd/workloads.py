@@ -24,6 +24,9 @@ Recipe (the same for every workload, seed 0 unless stated):
     Q = e4m3fn(clamp(R / scale, -448, 448)) with round-to-nearest-even.
     The clamp is needed because torch's cast does not saturate;
   * bias ~ N(0, 0.01^2).
+With q_format="e4m3fnuz" the residual's codes are e4m3fnuz instead, with
+scale = float32(max|R| / 240) and a clamp to +-240 (the format's largest
+value, so the largest |R| always lands on the codes 0x7F / 0xFF).
 """
 from __future__ import annotations
 
@@ -90,8 +93,25 @@ def quantize_e4m3fn(R: torch.Tensor):
     return codes.contiguous(), scale
 
 
+E4M3FNUZ_MAX = 240.0
+
+
+def quantize_e4m3fnuz(R: torch.Tensor):
+    """Per-tensor e4m3fnuz codes of a float32 tensor (the residual format the
+    LiteLinear README names for AMD hardware): (uint8 codes, scale), scale =
+    amax / 240, so the largest magnitude lands on the code of +-240 (0x7F or
+    0xFF).  Data generation only, with torch's cast (nearest even) after a
+    clamp to +-240."""
+    R = R.to(torch.float32)
+    amax = float(R.abs().max()) if R.numel() else 0.0
+    scale = float(np.float32(amax / E4M3FNUZ_MAX)) if amax > 0 else 1.0
+    q = torch.clamp(R / torch.tensor(scale, dtype=torch.float32), -E4M3FNUZ_MAX, E4M3FNUZ_MAX)
+    codes = q.to(torch.float8_e4m3fnuz).view(torch.uint8)
+    return codes.contiguous(), scale
+
+
 def make_inputs(w: Workload | str, seed: int = 0, *, M: int | None = None,
-                with_bias: bool = True) -> dict:
+                with_bias: bool = True, q_format: str = "e4m3fn") -> dict:
     """Draw one workload's inputs as CPU tensors.
 
     ``M`` overrides the row count (the other draws keep their order).  Returns
@@ -112,7 +132,7 @@ def make_inputs(w: Workload | str, seed: int = 0, *, M: int | None = None,
     B = g.standard_normal((r, K), dtype=np.float32) * np.float32(1.0 / np.sqrt(K)) if r else np.zeros((0, K), np.float32)
     R = g.standard_normal((N, K), dtype=np.float32) * np.float32(w.resid_sigma)
     bias = g.standard_normal((N,), dtype=np.float32) * np.float32(w.bias_sigma)
-    Q, scale = quantize_e4m3fn(torch.from_numpy(R))
+    Q, scale = (quantize_e4m3fnuz if q_format == "e4m3fnuz" else quantize_e4m3fn)(torch.from_numpy(R))
     return {
         "x": _bf16(x), "A": _bf16(A), "B": _bf16(B), "Q": Q, "scale": scale,
         "bias": _bf16(bias) if with_bias else None,
@@ -121,10 +141,10 @@ def make_inputs(w: Workload | str, seed: int = 0, *, M: int | None = None,
 
 
 def random_inputs(M: int, K: int, N: int, r: int, seed: int = 0, *,
-                  with_bias: bool = True, x_sigma: float = 1.0) -> dict:
+                  with_bias: bool = True, x_sigma: float = 1.0, q_format: str = "e4m3fn") -> dict:
     """Inputs of an arbitrary shape drawn with the same recipe (no outliers)."""
     w = Workload(f"adhoc_{M}x{K}x{N}_r{r}", M, K, N, r, x_sigma=x_sigma)
-    return make_inputs(w, seed, with_bias=with_bias)
+    return make_inputs(w, seed, with_bias=with_bias, q_format=q_format)
 
 
 def exact_inputs(M: int, K: int, N: int, r: int, seed: int = 0, *,
