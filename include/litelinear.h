@@ -52,9 +52,11 @@ typedef enum {
     LITELINEAR_ERR_UNSUPPORTED = 2, /* in % 16 != 0, or x / Q / B / y not 16-byte aligned */
     LITELINEAR_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
     LITELINEAR_ERR_OOM = 4,         /* workspace allocation failed */
-    LITELINEAR_ERR_SYNC = 5         /* an earlier launch on this handle gave up waiting for other
+    LITELINEAR_ERR_SYNC = 5,        /* an earlier launch on this handle gave up waiting for other
                                        work-groups of the launch: its output is undefined (see
                                        litelinear_device_status) */
+    LITELINEAR_ERR_SCRATCH = 6      /* litelinear_forward_noalloc: the call needs more workspace than
+                                       the fixed scratch holds (nothing was queued) */
 } litelinear_status_t;
 
 /* Options set per handle with litelinear_set_option(). */
@@ -186,6 +188,36 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h,
                                        const void *Q, float scale, const void *bias,
                                        void *y, int64_t M, int64_t in, int64_t out,
                                        int64_t r, hipStream_t stream);
+
+/*
+ * litelinear_forward() for callers that cannot allocate memory: code under
+ * HIP graph capture that must not add allocation nodes, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same kernels, options and results
+ * as litelinear_forward(), but the workspace (T' blocks, partial sums,
+ * counters, a padded copy of A, e4m3fn activations) is carved out of a
+ * fixed scratch array of 32 MiB per device, a file-scope device array of
+ * the library that each device holds until the process ends; the call
+ * allocates nothing (no hipMalloc, hipFree or event), and queues a small
+ * kernel that clears the counters it uses, then the forward.
+ *
+ *   Arguments, layouts and ownership as litelinear_forward().
+ *   Every call on one device shares that device's scratch: calls that can
+ *   overlap on one device (different streams, or different handles without
+ *   ordering between them) race and must be ordered by the caller.
+ *   The workspace needed: counters (at most 64 KiB), plus 2 M r_pad bytes of
+ *   T' (tiled path), up to 4 t_splits M r_pad bytes of T partial sums, for
+ *   the skinny path 4 splits M out bytes of partial sums, 2 out r_pad bytes
+ *   for a padded A, and M (in + 4) bytes with e4m3fn activations, each
+ *   rounded up to 256 bytes.
+ * Errors: those of litelinear_forward(), and SCRATCH (nothing queued) when
+ * the call needs more than the scratch holds (for example the 16384 x 4096
+ * e4m3fn-activation forward, whose activation codes alone take 64 MiB).
+ */
+litelinear_status_t litelinear_forward_noalloc(litelinear_handle_t h,
+                                               const void *x, const void *A, const void *B,
+                                               const void *Q, float scale, const void *bias,
+                                               void *y, int64_t M, int64_t in, int64_t out,
+                                               int64_t r, hipStream_t stream);
 
 /*
  * litelinear_forward() on activations whose rows are `ldx` elements apart:

@@ -80,6 +80,7 @@ struct litelinear_ctx {
     unsigned *err_host = nullptr;
     unsigned *err_dev = nullptr;
     bool sync_dirty = false;        // counters must be cleared before the next launch
+    void *scratch = nullptr;        // the device's fixed scratch (litelinear_forward_noalloc)
     int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0, opt_t_splits = 0, opt_act_fp8 = 0,
             opt_gelu = 0, opt_test_wait = 0, opt_q_format = 0;
     Prof prof[kNumKernels];
@@ -176,6 +177,7 @@ const char *litelinear_status_string(litelinear_status_t s) {
         case LITELINEAR_ERR_HIP: return "HIP runtime error";
         case LITELINEAR_ERR_OOM: return "out of device memory";
         case LITELINEAR_ERR_SYNC: return "a kernel's wait for other work-groups of its launch gave up (output undefined)";
+        case LITELINEAR_ERR_SCRATCH: return "the call needs more workspace than the fixed no-allocation scratch holds";
     }
     return "unknown status";
 }
@@ -248,6 +250,12 @@ litelinear_status_t litelinear_create(litelinear_handle_t *out, int device_ordin
     }
     *h->err_host = 0;
     h->err_dev = (unsigned *)dp;
+    if (ll::scratch_init(h->device, &h->scratch) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipHostFree(h->err_host);
+        delete h;
+        return LITELINEAR_ERR_HIP;
+    }
     *out = h;
     return LITELINEAR_OK;
 }
@@ -383,10 +391,36 @@ litelinear_status_t take_handle_ws(litelinear_ctx *h, const WsRequest &rq, hipSt
     return LITELINEAR_OK;
 }
 
+// The same request carved out of the device's fixed scratch (no
+// allocation): the counters at its start, every other buffer after them on
+// a 256-byte boundary.  SCRATCH when the call needs more than it holds.
+litelinear_status_t take_scratch_ws(litelinear_ctx *h, const WsRequest &rq, void *(&ptr)[WS_COUNT]) {
+    unsigned char *base = (unsigned char *)h->scratch;
+    if (!base) return LITELINEAR_ERR_HIP;
+    if (rq.need[WS_SYNC] > ll::kScratchSyncBytes) return LITELINEAR_ERR_SCRATCH;
+    size_t off = ll::kScratchSyncBytes;
+    for (int i = 0; i < WS_COUNT; ++i) {
+        ptr[i] = nullptr;
+        if (rq.need[i] == 0) continue;
+        if (i == WS_SYNC) {
+            ptr[i] = base;
+            continue;
+        }
+        const size_t bytes = (rq.need[i] + 255) & ~(size_t)255;
+        if (bytes > ll::kScratchBytes - off) return LITELINEAR_ERR_SCRATCH;
+        ptr[i] = base + off;
+        off += bytes;
+    }
+    return LITELINEAR_OK;
+}
+
 // The forward for one output, or for two sharing x and B (s2 != nullptr:
 // the tiled kernel, T computed once).  Arguments are already checked.
+// noalloc: the workspace comes from the device's fixed scratch, and the
+// counters this call uses are cleared on the stream first.
 litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, const void *B, const OutSet &s1,
-                                 const OutSet *s2, int64_t M, int64_t in, int64_t r, hipStream_t stream) {
+                                 const OutSet *s2, int64_t M, int64_t in, int64_t r, hipStream_t stream,
+                                 bool noalloc = false) {
     const void *A = s1.A, *Q = s1.Q, *bias = s1.bias;
     void *y = s1.y;
     const float scale = s1.scale;
@@ -395,6 +429,9 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
     litelinear_status_t st = LITELINEAR_OK;
     if (take_device_error(h)) return LITELINEAR_ERR_SYNC;
     const bool in_capture = capturing(stream);
+    // no event pairs under capture, nor in the no-allocation call (an event
+    // is an allocation of its own)
+    const bool no_events = in_capture || noalloc;
     const unsigned wait_limit = h->opt_test_wait > 0 ? (unsigned)h->opt_test_wait : kWaitLimit;
     const unsigned wait_extra = h->opt_test_wait > 0 ? 1u : 0u;
 
@@ -486,10 +523,16 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
     }
 
     void *ws[WS_COUNT];
-    st = take_handle_ws(h, rq, stream, in_capture, ws);
+    st = noalloc ? take_scratch_ws(h, rq, ws) : take_handle_ws(h, rq, stream, in_capture, ws);
     if (st != LITELINEAR_OK) return st;
-    // After a wait that gave up the counters may hold stale counts.
-    if (h->sync_dirty && h->ws[WS_SYNC].p) {
+    if (noalloc) {
+        // The scratch is shared by every call on the device: its counters
+        // are cleared for this call (a kernel, never a memset node).
+        if (rq.need[WS_SYNC] && ll::launch_fill_u32((unsigned *)ws[WS_SYNC], (int64_t)(rq.need[WS_SYNC] / 4), 0u,
+                                                    stream) != hipSuccess)
+            return LITELINEAR_ERR_HIP;
+    } else if (h->sync_dirty && h->ws[WS_SYNC].p) {
+        // After a wait that gave up the counters may hold stale counts.
         if (ll::launch_fill_u32((unsigned *)h->ws[WS_SYNC].p, (int64_t)(h->ws[WS_SYNC].bytes / 4), 0u, stream) !=
             hipSuccess)
             return LITELINEAR_ERR_HIP;
@@ -498,14 +541,14 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
 
     const void *a_eff = A;
     if (pad1) {
-        st = timed_launch(h, LITELINEAR_KERNEL_PAD_A, stream, in_capture,
+        st = timed_launch(h, LITELINEAR_KERNEL_PAD_A, stream, no_events,
                           [&] { return ll::launch_pad_a(A, ws[WS_APAD], out, r, r_pad, stream); });
         if (st != LITELINEAR_OK) return st;
         a_eff = ws[WS_APAD];
     }
     const void *a_eff2 = s2 ? s2->A : nullptr;
     if (pad2) {
-        st = timed_launch(h, LITELINEAR_KERNEL_PAD_A, stream, in_capture,
+        st = timed_launch(h, LITELINEAR_KERNEL_PAD_A, stream, no_events,
                           [&] { return ll::launch_pad_a(s2->A, ws[WS_APAD2], s2->out, r, r_pad, stream); });
         if (st != LITELINEAR_OK) return st;
         a_eff2 = ws[WS_APAD2];
@@ -535,14 +578,14 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
         sp.err = h->err_dev;
         sp.wait_limit = wait_limit;
         sp.wait_extra = wait_extra;
-        return timed_launch(h, LITELINEAR_KERNEL_SKINNY, stream, in_capture,
+        return timed_launch(h, LITELINEAR_KERNEL_SKINNY, stream, no_events,
                             [&] { return ll::launch_skinny(sp, a_eff, stream); });
     }
 
     if (act8) {
         p.xq = ws[WS_XQ];
         p.xs = (float *)ws[WS_XS];
-        st = timed_launch(h, LITELINEAR_KERNEL_QUANT, stream, in_capture,
+        st = timed_launch(h, LITELINEAR_KERNEL_QUANT, stream, no_events,
                           [&] { return ll::launch_quant_rows(x, ldx, ws[WS_XQ], (float *)ws[WS_XS], M, in, stream); });
         if (st != LITELINEAR_OK) return st;
     }
@@ -553,7 +596,7 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
     p.wait_limit = wait_limit;
     p.wait_extra = wait_extra;
     unsigned *sync = producers ? (unsigned *)ws[WS_SYNC] : nullptr;
-    return timed_launch(h, LITELINEAR_KERNEL_MAIN, stream, in_capture,
+    return timed_launch(h, LITELINEAR_KERNEL_MAIN, stream, no_events,
                         [&] { return ll::launch_tiled(p, mc, a_eff, a_eff2, sync, stream); });
 }
 
@@ -578,6 +621,19 @@ litelinear_status_t litelinear_forward(litelinear_handle_t h, const void *x, con
                                        const void *Q, float scale, const void *bias, void *y, int64_t M,
                                        int64_t in, int64_t out, int64_t r, hipStream_t stream) {
     return litelinear_forward_strided(h, x, in, A, B, Q, scale, bias, y, M, in, out, r, stream);
+}
+
+litelinear_status_t litelinear_forward_noalloc(litelinear_handle_t h, const void *x, const void *A, const void *B,
+                                               const void *Q, float scale, const void *bias, void *y, int64_t M,
+                                               int64_t in, int64_t out, int64_t r, hipStream_t stream) {
+    if (!h) return LITELINEAR_ERR_INVALID_ARG;
+    litelinear_status_t st =
+        check_args_ld(x, in, A, B, Q, bias, y, M, in, out, r, h->opt_out_f32 != 0 ? 4 : 2, h->opt_gelu == 2);
+    if (st != LITELINEAR_OK) return st;
+    if (M == 0 || out == 0) return LITELINEAR_OK;
+    DeviceGuard guard(h->device);
+    if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
+    return forward_impl(h, x, in, B, OutSet{A, Q, bias, scale, y, out}, nullptr, M, in, r, stream, true);
 }
 
 litelinear_status_t litelinear_forward_pair(litelinear_handle_t h, const void *x, const void *B, const void *A1,

@@ -64,6 +64,14 @@ hipError_t launch_residual_quant(const void *W, const void *A, const void *B, in
 hipError_t launch_read_probe(const void *src, int64_t bytes, int wgs, int unroll, bool nontemporal, unsigned *sink,
                              hipStream_t s);
 
+// Fixed device scratch of litelinear_forward_noalloc (noalloc.hip): a
+// file-scope device array of kScratchBytes per device.  scratch_init()
+// returns its device address on `device`, which must be the current device;
+// the address is looked up once per device and kept.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr size_t kScratchSyncBytes = (size_t)64 << 10;  // counters at its start
+hipError_t scratch_init(int device, void **ptr);
+
 // Tile configuration of one launch (work-group tile BM x BN).
 struct TileCfg {
     int bm, bn;

@@ -29,6 +29,7 @@ class Status(enum.IntEnum):
     HIP = 3
     OOM = 4
     SYNC = 5  # an earlier launch gave up waiting for other work-groups (see device_status)
+    SCRATCH = 6  # forward_noalloc: more workspace needed than the fixed scratch holds
 
 
 class Option(enum.IntEnum):
@@ -67,7 +68,7 @@ EXPORTS = ("litelinear_create", "litelinear_forward", "litelinear_destroy", "lit
            "litelinear_set_option", "litelinear_kernel_time", "litelinear_status_string",
            "litelinear_version", "litelinear_quantize_rows", "litelinear_quantize_tensor",
            "litelinear_residual_quantize", "litelinear_forward_pair", "litelinear_forward_strided",
-           "litelinear_device_status", "litelinear_read_probe")
+           "litelinear_device_status", "litelinear_read_probe", "litelinear_forward_noalloc")
 
 
 class LiteLinearError(RuntimeError):
@@ -94,6 +95,8 @@ def lib(path: str | None = None) -> ctypes.CDLL:
         L.litelinear_destroy.restype = ctypes.c_int
         L.litelinear_forward.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, i64, i64, i64, i64, vp]
         L.litelinear_forward.restype = ctypes.c_int
+        L.litelinear_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, i64, i64, i64, i64, vp]
+        L.litelinear_forward_noalloc.restype = ctypes.c_int
         L.litelinear_forward_strided.argtypes = [vp, vp, i64, vp, vp, vp, ctypes.c_float, vp, vp, i64, i64, i64,
                                                  i64, vp]
         L.litelinear_forward_strided.restype = ctypes.c_int
@@ -198,12 +201,15 @@ class Handle:
 
     def forward(self, x: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, Q: torch.Tensor,
                 scale: float, bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+                stream: torch.cuda.Stream | None = None, noalloc: bool = False) -> torch.Tensor:
         """y = (x B^T) A^T + scale * (x dec(Q)^T) + bias on this handle's device.
 
         x may be a row slice of a wider tensor (last dimension contiguous,
         rows evenly spaced after flattening the leading dimensions, e.g.
-        ``big[:, :in]``): it is then read in place with its row stride."""
+        ``big[:, :in]``): it is then read in place with its row stride.
+        ``noalloc``: litelinear_forward_noalloc (the workspace from the
+        library's fixed per-device scratch; contiguous x; pass ``out`` to
+        allocate nothing on this side either)."""
         dev = self.device
         if Q.dtype in (torch.float8_e4m3fn, torch.float8_e4m3fnuz):
             Q = Q.view(torch.uint8)
@@ -249,7 +255,13 @@ class Handle:
             if out.numel() != M * y_cols:
                 raise ValueError("out has the wrong number of elements")
         s = _stream_ptr(stream, dev)
-        if ldx == in_features:
+        if noalloc:
+            if ldx != in_features:
+                raise ValueError("forward_noalloc takes contiguous rows of x")
+            st = lib().litelinear_forward_noalloc(self._h, _ptr(x2), _ptr(A) if r else None, _ptr(B) if r else None,
+                                                  _ptr(Q), float(scale), _ptr(bias), _ptr(out), M, in_features,
+                                                  out_features, r, s)
+        elif ldx == in_features:
             st = lib().litelinear_forward(self._h, _ptr(x2), _ptr(A) if r else None, _ptr(B) if r else None,
                                           _ptr(Q), float(scale), _ptr(bias), _ptr(out), M, in_features,
                                           out_features, r, s)
