@@ -61,11 +61,16 @@ typedef enum {
 
 /* Options set per handle with litelinear_set_option(). */
 typedef enum {
-    /* Kernel family.  0 = choose from M (default: skinny for M <= 64, but
-     * for tiny problems, 32 < M, in <= 256 and M * in * out <= 2^22, where
-     * the tiled kernel computes T inside each output tile); 1 = the skinny split-K
-     * kernel (HBM-bound on Q, for small M); 2 = the tiled kernel (MFMA-bound,
-     * for large M).  Both compute the same operation. */
+    /* Kernel family.  0 = choose from the shape (default): the stream kernel
+     * where it applies (M <= 16 and at least 128 work-groups of 32 output
+     * columns), else the skinny kernel for M <= 64 (but for tiny problems,
+     * 32 < M, in <= 256 and M * in * out <= 2^22, where the tiled kernel
+     * computes T inside each output tile), else the tiled kernel;
+     * 1 = the skinny split-K kernel (HBM-bound on Q, for small M); 2 = the
+     * tiled kernel (MFMA-bound, for large M); 3 = the stream kernel (M <=
+     * 16: each work-group streams Q for 32 columns over all of `in`, T from
+     * producer work-groups beside it).  All compute the same operation; a
+     * kernel that does not take the shape returns UNSUPPORTED. */
     LITELINEAR_OPT_PATH = 1,
     /* Output type.  0 = bf16 y (default, rounded to nearest even);
      * 1 = float32 y [M, out] (no output rounding; y must hold 4*M*out bytes). */
@@ -138,7 +143,7 @@ typedef enum {
     LITELINEAR_KERNEL_PAD_A = 0,  /* copy of A into a zero-padded [out, r_pad] buffer (either path,
                                      only when r % 8 != 0 or A is not 16-byte aligned) */
     LITELINEAR_KERNEL_MAIN = 1,   /* tiled path: T = x B^T, residual, rank-r product and bias */
-    LITELINEAR_KERNEL_SKINNY = 2, /* skinny path: the same in one launch of its own kernel */
+    LITELINEAR_KERNEL_SKINNY = 2, /* skinny and stream paths: the same in one launch of their own kernel */
     LITELINEAR_KERNEL_QUANT = 3,  /* activations to e4m3fn (LITELINEAR_OPT_ACT_FP8, litelinear_quantize_rows) */
     LITELINEAR_KERNEL_CONVERT = 4 /* decomposition side: litelinear_quantize_tensor, litelinear_residual_quantize
                                      (both passes of one call count as one launch) */

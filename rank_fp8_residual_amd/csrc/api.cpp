@@ -288,7 +288,7 @@ litelinear_status_t litelinear_set_option(litelinear_handle_t h, int key, int64_
     if (!h) return LITELINEAR_ERR_INVALID_ARG;
     switch (key) {
         case LITELINEAR_OPT_PATH:
-            if (value < 0 || value > 2) return LITELINEAR_ERR_INVALID_ARG;
+            if (value < 0 || value > 3) return LITELINEAR_ERR_INVALID_ARG;
             h->opt_path = value;
             return LITELINEAR_OK;
         case LITELINEAR_OPT_OUTPUT_F32:
@@ -453,9 +453,15 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
         ll::skinny_shape_ok(M, in, out, r_pad, plan = ll::skinny_plan(M, in, out, r_pad, h->opt_split), ldx) &&
         (!glu || (out * in < lim31 && out * (r_pad > 0 ? r_pad : 1) * 2 < lim31 &&
                   (int64_t)plan.splits * M * plan.tiles_n * 128 * 4 < lim31));
+    const bool stream_ok = !act8 && in > 0 && ll::stream_supports(M, in, out, r_pad, glu, ldx);
     if (s2) path = 2;
-    if (path == 0) path = (M <= kSkinnyAutoMaxM && skinny_ok && !ll::tiled_tiny_shape(M, in, out, r)) ? 1 : 2;
-    if (path == 1 && !skinny_ok) return LITELINEAR_ERR_UNSUPPORTED;
+    if (path == 0) {
+        if (stream_ok)
+            path = 3;
+        else
+            path = (M <= kSkinnyAutoMaxM && skinny_ok && !ll::tiled_tiny_shape(M, in, out, r)) ? 1 : 2;
+    }
+    if ((path == 1 && !skinny_ok) || (path == 3 && !stream_ok)) return LITELINEAR_ERR_UNSUPPORTED;
 
     // Workspace of this call.  A whose rows are not whole 16-byte chunks is
     // first copied into a zero-padded [out, r_pad] buffer (both paths read A
@@ -466,10 +472,17 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
     if (pad2) rq.need[WS_APAD2] = (size_t)s2->out * r_pad * 2;
 
     ll::SkinnyProblem sp{};
+    ll::StreamProblem xp{};
     ll::TiledProblem p{};
     ll::TileCfg mc{};
     bool producers = false;
-    if (path == 1) {
+    if (path == 3) {
+        if (r > 0) {
+            rq.need[WS_TWS] = (size_t)ll::stream_t_bytes(r_pad);
+            rq.need[WS_TPART] = (size_t)ll::stream_piece_bytes(r_pad);
+            rq.need[WS_SYNC] = (size_t)ll::stream_sync_words(r_pad) * sizeof(unsigned);
+        }
+    } else if (path == 1) {
         sp.plan = plan;
         // partial sums' rows: the products' columns (whole column tiles with
         // the gated epilogue)
@@ -554,6 +567,33 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
         a_eff2 = ws[WS_APAD2];
     }
 
+    if (path == 3) {
+        xp.x = x;
+        xp.ldx = ldx;
+        xp.A = A;
+        xp.B = B;
+        xp.Q = Q;
+        xp.bias = bias;
+        xp.y = y;
+        xp.scale = scale;
+        xp.M = M;
+        xp.K = in;
+        xp.N = out;
+        xp.r = r;
+        xp.r_pad = r_pad;
+        xp.out_f32 = out_f32;
+        xp.gelu = h->opt_gelu == 1;
+        xp.glu = glu;
+        xp.q_format = q_format;
+        xp.t = ws[WS_TWS];
+        xp.t_piece = (float *)ws[WS_TPART];
+        xp.sync = (unsigned *)ws[WS_SYNC];
+        xp.err = h->err_dev;
+        xp.wait_limit = wait_limit;
+        xp.wait_extra = wait_extra;
+        return timed_launch(h, LITELINEAR_KERNEL_SKINNY, stream, no_events,
+                            [&] { return ll::launch_stream(xp, a_eff, stream); });
+    }
     if (path == 1) {
         sp.x = x;
         sp.ldx = ldx;
@@ -660,7 +700,8 @@ litelinear_status_t litelinear_forward_pair(litelinear_handle_t h, const void *x
     const OutSet s1{A1, Q1, bias1, scale1, y1, out1}, s2{A2, Q2, bias2, scale2, y2, out2};
     // One output empty, or the skinny regime (where T is a small part of
     // the time): one forward per output.  Otherwise one tiled launch.
-    const bool skinny = h->opt_path == 1 || (h->opt_path == 0 && M <= kSkinnyAutoMaxM && h->opt_act_fp8 == 0);
+    const bool skinny =
+        h->opt_path == 1 || h->opt_path == 3 || (h->opt_path == 0 && M <= kSkinnyAutoMaxM && h->opt_act_fp8 == 0);
     if (out1 == 0 || out2 == 0 || in == 0 || skinny) {
         if (out1 > 0 && (st = forward_impl(h, x, in, B, s1, nullptr, M, in, r, stream)) != LITELINEAR_OK) return st;
         if (out2 > 0) st = forward_impl(h, x, in, B, s2, nullptr, M, in, r, stream);

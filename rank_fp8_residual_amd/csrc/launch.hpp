@@ -148,6 +148,29 @@ struct SkinnyProblem {
     SkinnyPlan plan;
 };
 
+// Stream path (M <= 16 rows, wide outputs; see stream.hip): T producers
+// plus one work-group per 32 columns of the products over all of K.
+struct StreamProblem {
+    const void *x, *A, *B, *Q, *bias;
+    void *y;
+    void *t;             // T bf16 [16, r_pad] (r > 0)
+    float *t_piece;      // stream_piece_bytes(r_pad) of T pieces (r > 0)
+    unsigned *sync;      // stream_sync_words(r_pad) counters, zero before and after the launch
+    unsigned *err;       // host-visible error word (a bounded wait gave up)
+    unsigned wait_limit, wait_extra;
+    float scale;
+    int64_t M, K, N, r, r_pad;
+    int64_t ldx;
+    bool out_f32, gelu;
+    int q_format;
+    bool glu;            // gated epilogue: N = 2F rows of Q, A, bias; y [M, F]
+};
+bool stream_supports(int64_t M, int64_t K, int64_t N, int64_t r_pad, bool glu, int64_t ldx);
+int64_t stream_sync_words(int64_t r_pad);
+int64_t stream_piece_bytes(int64_t r_pad);
+int64_t stream_t_bytes(int64_t r_pad);
+hipError_t launch_stream(const StreamProblem &p, const void *a_eff, hipStream_t s);
+
 bool skinny_supports(int64_t M);  // row counts the skinny kernel takes
 // splits_hint > 0 asks for about that many K slices.
 SkinnyPlan skinny_plan(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t splits_hint);

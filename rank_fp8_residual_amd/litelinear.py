@@ -54,6 +54,7 @@ class Path(enum.IntEnum):
     AUTO = 0
     SKINNY = 1
     TILED = 2
+    STREAM = 3
 
 
 class Kernel(enum.IntEnum):

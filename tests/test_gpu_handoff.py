@@ -52,6 +52,7 @@ CAPTURE_CASES = [
     (600, 1024, 1024, 256, Path.TILED, False),
     (300, 1280, 520, 80, Path.TILED, False),
     (16, 2048, 4096, 64, Path.SKINNY, False),
+    (16, 2048, 8192, 128, Path.STREAM, False),
     (1024, 512, 2048, 64, Path.TILED, True),
 ]
 
@@ -114,7 +115,7 @@ def test_capture_refuses_to_grow_the_workspace(dev):
 # 256-column T blocks, a pair, the skinny kernel (one and several slices)
 TIMEOUT_CASES = [
     (1024, 512, 2048, 64, Path.TILED), (300, 1280, 520, 80, Path.TILED), (600, 1024, 1024, 256, Path.TILED),
-    (16, 2048, 4096, 64, Path.SKINNY), (40, 512, 640, 32, Path.SKINNY),
+    (16, 2048, 4096, 64, Path.SKINNY), (40, 512, 640, 32, Path.SKINNY), (16, 2048, 8192, 128, Path.STREAM),
 ]
 
 
