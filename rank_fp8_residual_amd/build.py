@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "liblitelinear.so")
 ARCH = "gfx950"
-SOURCES = ["tiled.hip", "skinny.hip", "stream.hip", "quant.hip", "convert.hip", "probe.hip", "noalloc.hip", "api.cpp"]
+SOURCES = ["tiled.hip", "skinny.hip", "stream.hip", "quant.hip", "convert.hip", "probe.hip", "noalloc.hip", "check.cpp", "api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

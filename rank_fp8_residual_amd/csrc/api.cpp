@@ -10,6 +10,7 @@
 #include <utility>
 #include <vector>
 
+#include "check.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -42,13 +43,8 @@ struct DeviceGuard {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
-    if (!a || !b || na == 0 || nb == 0) return false;
-    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-    return a0 < b0 + nb && b0 < a0 + na;
-}
-
-bool aligned(const void *p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+using ll::aligned;
+using ll::overlaps;
 
 }  // namespace
 
@@ -180,50 +176,6 @@ const char *litelinear_status_string(litelinear_status_t s) {
         case LITELINEAR_ERR_SCRATCH: return "the call needs more workspace than the fixed no-allocation scratch holds";
     }
     return "unknown status";
-}
-
-namespace {
-
-// litelinear_check_args() for x rows ldx elements apart.
-litelinear_status_t check_args_ld(const void *x, int64_t ldx, const void *A, const void *B, const void *Q,
-                                  const void *bias, const void *y, int64_t M, int64_t in, int64_t out, int64_t r,
-                                  int y_bytes_per_elem, bool glu = false) {
-    const int64_t lim = (int64_t)1 << 40;
-    if (M < 0 || in < 0 || out < 0 || r < 0) return LITELINEAR_ERR_INVALID_ARG;
-    if (ldx < in || ldx > lim || (double)M * (double)ldx > 4.0e18) return LITELINEAR_ERR_INVALID_ARG;
-    if (y_bytes_per_elem != 2 && y_bytes_per_elem != 4) return LITELINEAR_ERR_INVALID_ARG;
-    if (M > lim || in > lim || out > lim || r > lim) return LITELINEAR_ERR_INVALID_ARG;
-    if ((double)M * (double)in > 4.0e18 || (double)M * (double)out > 1.0e18 ||
-        (double)out * (double)in > 4.0e18 || (double)r * (double)(in + out) > 4.0e18)
-        return LITELINEAR_ERR_INVALID_ARG;
-    if (M == 0 || out == 0) return LITELINEAR_OK;  // nothing to compute
-    if (!y) return LITELINEAR_ERR_INVALID_ARG;
-    if (in > 0 && (!x || !Q)) return LITELINEAR_ERR_INVALID_ARG;
-    if (r > 0 && (!A || (in > 0 && !B))) return LITELINEAR_ERR_INVALID_ARG;
-    if (in % 16 != 0) return LITELINEAR_ERR_UNSUPPORTED;
-    if (in > 0 && (!aligned(x, 16) || !aligned(Q, 16) || ldx % 8 != 0)) return LITELINEAR_ERR_UNSUPPORTED;
-    if (r > 0 && in > 0 && !aligned(B, 16)) return LITELINEAR_ERR_UNSUPPORTED;
-    if (r > 0 && !aligned(A, 2)) return LITELINEAR_ERR_UNSUPPORTED;
-    if (bias && !aligned(bias, 2)) return LITELINEAR_ERR_UNSUPPORTED;
-    if (!aligned(y, (uintptr_t)y_bytes_per_elem)) return LITELINEAR_ERR_UNSUPPORTED;
-    // the gated epilogue writes half as many columns as Q has rows
-    if (glu && out % 2 != 0) return LITELINEAR_ERR_INVALID_ARG;
-    const uint64_t ny = (uint64_t)M * (uint64_t)(glu ? out / 2 : out) * (uint64_t)y_bytes_per_elem;
-    // x's extent: M - 1 row strides and one row
-    const uint64_t nx = in > 0 ? ((uint64_t)(M - 1) * (uint64_t)ldx + (uint64_t)in) * 2 : 0;
-    if (overlaps(y, ny, x, nx) || overlaps(y, ny, Q, (uint64_t)out * in) ||
-        (r > 0 && (overlaps(y, ny, A, (uint64_t)out * r * 2) || overlaps(y, ny, B, (uint64_t)r * in * 2))) ||
-        overlaps(y, ny, bias, (uint64_t)out * 2))
-        return LITELINEAR_ERR_INVALID_ARG;
-    return LITELINEAR_OK;
-}
-
-}  // namespace
-
-litelinear_status_t litelinear_check_args(const void *x, const void *A, const void *B, const void *Q,
-                                          const void *bias, const void *y, int64_t M, int64_t in,
-                                          int64_t out, int64_t r, int y_bytes_per_elem) {
-    return check_args_ld(x, in, A, B, Q, bias, y, M, in, out, r, y_bytes_per_elem);
 }
 
 litelinear_status_t litelinear_create(litelinear_handle_t *out, int device_ordinal) {
@@ -649,7 +601,7 @@ litelinear_status_t litelinear_forward_strided(litelinear_handle_t h, const void
                                                int64_t M, int64_t in, int64_t out, int64_t r, hipStream_t stream) {
     if (!h) return LITELINEAR_ERR_INVALID_ARG;
     const bool out_f32 = h->opt_out_f32 != 0;
-    litelinear_status_t st = check_args_ld(x, ldx, A, B, Q, bias, y, M, in, out, r, out_f32 ? 4 : 2, h->opt_gelu == 2);
+    litelinear_status_t st = ll::check_args_ld(x, ldx, A, B, Q, bias, y, M, in, out, r, out_f32 ? 4 : 2, h->opt_gelu == 2);
     if (st != LITELINEAR_OK) return st;
     if (M == 0 || out == 0) return LITELINEAR_OK;
     DeviceGuard guard(h->device);
@@ -668,7 +620,7 @@ litelinear_status_t litelinear_forward_noalloc(litelinear_handle_t h, const void
                                                int64_t in, int64_t out, int64_t r, hipStream_t stream) {
     if (!h) return LITELINEAR_ERR_INVALID_ARG;
     litelinear_status_t st =
-        check_args_ld(x, in, A, B, Q, bias, y, M, in, out, r, h->opt_out_f32 != 0 ? 4 : 2, h->opt_gelu == 2);
+        ll::check_args_ld(x, in, A, B, Q, bias, y, M, in, out, r, h->opt_out_f32 != 0 ? 4 : 2, h->opt_gelu == 2);
     if (st != LITELINEAR_OK) return st;
     if (M == 0 || out == 0) return LITELINEAR_OK;
     DeviceGuard guard(h->device);

@@ -34,10 +34,10 @@ def to_dev(d, dev):
     return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
 
 
-def handle(dev, path=Path.STREAM, **opts):
+def handle(dev, path=Path.STREAM, opts=None):
     h = Handle(dev.index)
     h.set_option(Option.PATH, int(path))
-    for k, v in opts.items():
+    for k, v in (opts or {}).items():
         h.set_option(k, v)
     return h
 
@@ -60,7 +60,7 @@ def test_stream_parity(dev, shape, out_f32):
     M, K, N, r = shape
     d = wl.random_inputs(M, K, N, r, seed=900 + M + r)
     say("stream", shape, "f32" if out_f32 else "bf16")
-    h = handle(dev, **{Option.OUTPUT_F32: int(out_f32)})
+    h = handle(dev, opts={Option.OUTPUT_F32: int(out_f32)})
     g = to_dev(d, dev)
     y1 = fwd(h, g)
     y2 = fwd(h, g)
@@ -88,7 +88,7 @@ def test_stream_variants(dev, variant):
     if variant.endswith("geglu"):
         opts[Option.ACTIVATION] = int(Activation.GEGLU)
     say("stream variant", variant)
-    y = parity.to_f64(fwd(handle(dev, **opts), to_dev(d, dev)))
+    y = parity.to_f64(fwd(handle(dev, opts=opts), to_dev(d, dev)))
     v_ref = oracle.forward(d["x"], d["A"], d["B"], d["Q"], d["scale"], d["bias"],
                            q_format="e4m3fnuz" if fnuz else "e4m3fn")
     if variant == "gelu":
