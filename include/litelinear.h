@@ -61,16 +61,16 @@ typedef enum {
 
 /* Options set per handle with litelinear_set_option(). */
 typedef enum {
-    /* Kernel family.  0 = choose from the shape (default): the stream kernel
-     * where it applies (M <= 16 and at least 128 work-groups of 32 output
-     * columns), else the skinny kernel for M <= 64 (but for tiny problems,
-     * 32 < M, in <= 256 and M * in * out <= 2^22, where the tiled kernel
-     * computes T inside each output tile), else the tiled kernel;
-     * 1 = the skinny split-K kernel (HBM-bound on Q, for small M); 2 = the
-     * tiled kernel (MFMA-bound, for large M); 3 = the stream kernel (M <=
-     * 16: each work-group streams Q for 32 columns over all of `in`, T from
-     * producer work-groups beside it).  All compute the same operation; a
-     * kernel that does not take the shape returns UNSUPPORTED. */
+    /* Kernel family.  0 = choose from the shape (default): the skinny
+     * kernels for M <= 64 (but for tiny problems, 32 < M, in <= 256 and
+     * M * in * out <= 2^22, where the tiled kernel computes T inside each
+     * output tile), else the tiled kernel; 1 = the skinny kernels (HBM-bound
+     * on Q, for small M: up to 16 rows with 2048 < in <= 8192 and at least
+     * 192 groups of 32 output columns, and no K-split hint, each work-group
+     * streams its columns over all of `in`; otherwise work-groups split `in`
+     * into slices whose partial sums the last one of each column tile adds);
+     * 2 = the tiled kernel (MFMA-bound, for large M).  All compute the same
+     * operation; a kernel that does not take the shape returns UNSUPPORTED. */
     LITELINEAR_OPT_PATH = 1,
     /* Output type.  0 = bf16 y (default, rounded to nearest even);
      * 1 = float32 y [M, out] (no output rounding; y must hold 4*M*out bytes). */

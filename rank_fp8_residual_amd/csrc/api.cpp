@@ -59,6 +59,8 @@ enum WsBuf {
     WS_XQ,         // fp8-activation mode: e4m3fn codes of x [M, in]
     WS_XS,         // ... and the rows' scales [M]
     WS_SYNC,       // counters: zero before and after every launch
+    WS_GEN,        // skinny all-of-K kernel: two 64-bit counters that only grow
+                   // (zero when allocated or cleared after a failed wait)
     WS_COUNT
 };
 
@@ -240,7 +242,7 @@ litelinear_status_t litelinear_set_option(litelinear_handle_t h, int key, int64_
     if (!h) return LITELINEAR_ERR_INVALID_ARG;
     switch (key) {
         case LITELINEAR_OPT_PATH:
-            if (value < 0 || value > 3) return LITELINEAR_ERR_INVALID_ARG;
+            if (value < 0 || value > 2) return LITELINEAR_ERR_INVALID_ARG;
             h->opt_path = value;
             return LITELINEAR_OK;
         case LITELINEAR_OPT_OUTPUT_F32:
@@ -336,7 +338,7 @@ litelinear_status_t take_handle_ws(litelinear_ctx *h, const WsRequest &rq, hipSt
     for (int i = 0; i < WS_COUNT; ++i) {
         ptr[i] = nullptr;
         if (rq.need[i] == 0) continue;
-        const litelinear_status_t st = grow(h->ws[i], rq.need[i], i == WS_SYNC, s, in_capture);
+        const litelinear_status_t st = grow(h->ws[i], rq.need[i], i == WS_SYNC || i == WS_GEN, s, in_capture);
         if (st != LITELINEAR_OK) return st;
         ptr[i] = h->ws[i].p;
     }
@@ -402,18 +404,12 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
     const int64_t lim31 = (int64_t)1 << 31;
     const bool skinny_ok =
         !act8 && in > 0 && ll::skinny_supports(M) &&
-        ll::skinny_shape_ok(M, in, out, r_pad, plan = ll::skinny_plan(M, in, out, r_pad, h->opt_split), ldx) &&
+        ll::skinny_shape_ok(M, in, out, r_pad, plan = ll::skinny_plan(M, in, out, r_pad, h->opt_split, glu), ldx) &&
         (!glu || (out * in < lim31 && out * (r_pad > 0 ? r_pad : 1) * 2 < lim31 &&
                   (int64_t)plan.splits * M * plan.tiles_n * 128 * 4 < lim31));
-    const bool stream_ok = !act8 && in > 0 && ll::stream_supports(M, in, out, r_pad, glu, ldx);
     if (s2) path = 2;
-    if (path == 0) {
-        if (stream_ok)
-            path = 3;
-        else
-            path = (M <= kSkinnyAutoMaxM && skinny_ok && !ll::tiled_tiny_shape(M, in, out, r)) ? 1 : 2;
-    }
-    if ((path == 1 && !skinny_ok) || (path == 3 && !stream_ok)) return LITELINEAR_ERR_UNSUPPORTED;
+    if (path == 0) path = (M <= kSkinnyAutoMaxM && skinny_ok && !ll::tiled_tiny_shape(M, in, out, r)) ? 1 : 2;
+    if (path == 1 && !skinny_ok) return LITELINEAR_ERR_UNSUPPORTED;
 
     // Workspace of this call.  A whose rows are not whole 16-byte chunks is
     // first copied into a zero-padded [out, r_pad] buffer (both paths read A
@@ -424,17 +420,10 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
     if (pad2) rq.need[WS_APAD2] = (size_t)s2->out * r_pad * 2;
 
     ll::SkinnyProblem sp{};
-    ll::StreamProblem xp{};
     ll::TiledProblem p{};
     ll::TileCfg mc{};
     bool producers = false;
-    if (path == 3) {
-        if (r > 0) {
-            rq.need[WS_TWS] = (size_t)ll::stream_t_bytes(r_pad);
-            rq.need[WS_TPART] = (size_t)ll::stream_piece_bytes(r_pad);
-            rq.need[WS_SYNC] = (size_t)ll::stream_sync_words(r_pad) * sizeof(unsigned);
-        }
-    } else if (path == 1) {
+    if (path == 1) {
         sp.plan = plan;
         // partial sums' rows: the products' columns (whole column tiles with
         // the gated epilogue)
@@ -442,6 +431,8 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
         if (plan.splits > 1) rq.need[WS_PARTIALS] = (size_t)plan.splits * M * pcols * sizeof(float);
         if (r > 0) rq.need[WS_TPART] = (size_t)plan.t_splits * M * r_pad * sizeof(float);
         rq.need[WS_SYNC] = (size_t)ll::skinny_sync_words(plan) * sizeof(unsigned);
+        // (the piece count and 32 ticket counters, 256 bytes apart)
+        if (plan.fullk && r > 0) rq.need[WS_GEN] = 33 * 256;
     } else {
         p.x = x;
         p.ldx = ldx;
@@ -493,14 +484,16 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
     if (noalloc) {
         // The scratch is shared by every call on the device: its counters
         // are cleared for this call (a kernel, never a memset node).
-        if (rq.need[WS_SYNC] && ll::launch_fill_u32((unsigned *)ws[WS_SYNC], (int64_t)(rq.need[WS_SYNC] / 4), 0u,
-                                                    stream) != hipSuccess)
-            return LITELINEAR_ERR_HIP;
-    } else if (h->sync_dirty && h->ws[WS_SYNC].p) {
+        for (int i : {(int)WS_SYNC, (int)WS_GEN})
+            if (rq.need[i] && ll::launch_fill_u32((unsigned *)ws[i], (int64_t)(rq.need[i] / 4), 0u, stream) !=
+                                  hipSuccess)
+                return LITELINEAR_ERR_HIP;
+    } else if (h->sync_dirty) {
         // After a wait that gave up the counters may hold stale counts.
-        if (ll::launch_fill_u32((unsigned *)h->ws[WS_SYNC].p, (int64_t)(h->ws[WS_SYNC].bytes / 4), 0u, stream) !=
-            hipSuccess)
-            return LITELINEAR_ERR_HIP;
+        for (int i : {(int)WS_SYNC, (int)WS_GEN})
+            if (h->ws[i].p &&
+                ll::launch_fill_u32((unsigned *)h->ws[i].p, (int64_t)(h->ws[i].bytes / 4), 0u, stream) != hipSuccess)
+                return LITELINEAR_ERR_HIP;
         h->sync_dirty = false;
     }
 
@@ -519,33 +512,6 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
         a_eff2 = ws[WS_APAD2];
     }
 
-    if (path == 3) {
-        xp.x = x;
-        xp.ldx = ldx;
-        xp.A = A;
-        xp.B = B;
-        xp.Q = Q;
-        xp.bias = bias;
-        xp.y = y;
-        xp.scale = scale;
-        xp.M = M;
-        xp.K = in;
-        xp.N = out;
-        xp.r = r;
-        xp.r_pad = r_pad;
-        xp.out_f32 = out_f32;
-        xp.gelu = h->opt_gelu == 1;
-        xp.glu = glu;
-        xp.q_format = q_format;
-        xp.t = ws[WS_TWS];
-        xp.t_piece = (float *)ws[WS_TPART];
-        xp.sync = (unsigned *)ws[WS_SYNC];
-        xp.err = h->err_dev;
-        xp.wait_limit = wait_limit;
-        xp.wait_extra = wait_extra;
-        return timed_launch(h, LITELINEAR_KERNEL_SKINNY, stream, no_events,
-                            [&] { return ll::launch_stream(xp, a_eff, stream); });
-    }
     if (path == 1) {
         sp.x = x;
         sp.ldx = ldx;
@@ -567,6 +533,7 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
         sp.partials = (float *)ws[WS_PARTIALS];
         sp.t_part = (float *)ws[WS_TPART];
         sp.sync = (unsigned *)ws[WS_SYNC];
+        sp.gen = (unsigned long long *)ws[WS_GEN];
         sp.err = h->err_dev;
         sp.wait_limit = wait_limit;
         sp.wait_extra = wait_extra;
@@ -653,7 +620,7 @@ litelinear_status_t litelinear_forward_pair(litelinear_handle_t h, const void *x
     // One output empty, or the skinny regime (where T is a small part of
     // the time): one forward per output.  Otherwise one tiled launch.
     const bool skinny =
-        h->opt_path == 1 || h->opt_path == 3 || (h->opt_path == 0 && M <= kSkinnyAutoMaxM && h->opt_act_fp8 == 0);
+        h->opt_path == 1 || (h->opt_path == 0 && M <= kSkinnyAutoMaxM && h->opt_act_fp8 == 0);
     if (out1 == 0 || out2 == 0 || in == 0 || skinny) {
         if (out1 > 0 && (st = forward_impl(h, x, in, B, s1, nullptr, M, in, r, stream)) != LITELINEAR_OK) return st;
         if (out2 > 0) st = forward_impl(h, x, in, B, s2, nullptr, M, in, r, stream);

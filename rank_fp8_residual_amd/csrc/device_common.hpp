@@ -248,6 +248,22 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// A compile-time integer, and a loop over B .. E - 1 that calls f(CInt<i>{})
+// for each i: the loop is always unrolled, whatever the size of its body,
+// so that the body can use i as a constant (template arguments, register
+// array indices).
+template <int I>
+struct CInt {
+    static constexpr int value = I;
+};
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(CInt<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // Work-group barrier without a memory fence (loads may stay in flight).
 __device__ __forceinline__ void barrier_nofence() { __builtin_amdgcn_s_barrier(); }
 

@@ -126,6 +126,8 @@ struct SkinnyPlan {
     int pps;         // T pieces per K slice
     int pwg;         // work-groups per slice that compute pieces
     int producers;   // pwg * splits when r > 0: the pieces' work-groups
+    int fullk;       // 1: all of K per 32-column work-group (skinny_fullk_kernel)
+    int nq;          // fullk: ring stages per wave (K quarter = 256 nq)
 };
 
 struct SkinnyProblem {
@@ -134,6 +136,8 @@ struct SkinnyProblem {
     float *partials;     // float32 [splits, M, N] (splits > 1)
     unsigned *sync;      // skinny_sync_words() counters, zero before the
                          // launch and left at zero by it
+    unsigned long long *gen;  // plan.fullk and r > 0: 33 x 256 bytes of counters
+                              // that only grow (zero when allocated)
     unsigned *err;       // host-visible error word (a bounded wait gave up)
     unsigned wait_limit; // polls before a bounded wait gives up (> 0)
     unsigned wait_extra; // added to the T wait's target (1: a test of the error path)
@@ -148,32 +152,10 @@ struct SkinnyProblem {
     SkinnyPlan plan;
 };
 
-// Stream path (M <= 16 rows, wide outputs; see stream.hip): T producers
-// plus one work-group per 32 columns of the products over all of K.
-struct StreamProblem {
-    const void *x, *A, *B, *Q, *bias;
-    void *y;
-    void *t;             // T bf16 [16, r_pad] (r > 0)
-    float *t_piece;      // stream_piece_bytes(r_pad) of T pieces (r > 0)
-    unsigned *sync;      // stream_sync_words(r_pad) counters, zero before and after the launch
-    unsigned *err;       // host-visible error word (a bounded wait gave up)
-    unsigned wait_limit, wait_extra;
-    float scale;
-    int64_t M, K, N, r, r_pad;
-    int64_t ldx;
-    bool out_f32, gelu;
-    int q_format;
-    bool glu;            // gated epilogue: N = 2F rows of Q, A, bias; y [M, F]
-};
-bool stream_supports(int64_t M, int64_t K, int64_t N, int64_t r_pad, bool glu, int64_t ldx);
-int64_t stream_sync_words(int64_t r_pad);
-int64_t stream_piece_bytes(int64_t r_pad);
-int64_t stream_t_bytes(int64_t r_pad);
-hipError_t launch_stream(const StreamProblem &p, const void *a_eff, hipStream_t s);
-
 bool skinny_supports(int64_t M);  // row counts the skinny kernel takes
 // splits_hint > 0 asks for about that many K slices.
-SkinnyPlan skinny_plan(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t splits_hint);
+// glu: N counts the rows of Q (hidden and gate).
+SkinnyPlan skinny_plan(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t splits_hint, bool glu);
 int64_t skinny_sync_words(const SkinnyPlan &pl);
 // ldx: elements between rows of x.
 bool skinny_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r_pad, const SkinnyPlan &pl, int64_t ldx);

@@ -54,7 +54,6 @@ class Path(enum.IntEnum):
     AUTO = 0
     SKINNY = 1
     TILED = 2
-    STREAM = 3
 
 
 class Kernel(enum.IntEnum):

@@ -46,13 +46,14 @@ def oracle_y(d):
 
 
 # (M, in, out, r, path, act8): the tiled kernel with T producers (64- and
-# 256-column T blocks, K-sliced T), the skinny kernel, the fp8-activation mode
+# 256-column T blocks, K-sliced T), the skinny kernels (K-sliced, and all of
+# K per work-group), the fp8-activation mode
 CAPTURE_CASES = [
     (1024, 512, 2048, 64, Path.TILED, False),
     (600, 1024, 1024, 256, Path.TILED, False),
     (300, 1280, 520, 80, Path.TILED, False),
     (16, 2048, 4096, 64, Path.SKINNY, False),
-    (16, 2048, 8192, 128, Path.STREAM, False),
+    (16, 4096, 8192, 64, Path.SKINNY, False),
     (1024, 512, 2048, 64, Path.TILED, True),
 ]
 
@@ -112,10 +113,12 @@ def test_capture_refuses_to_grow_the_workspace(dev):
 
 
 # (M, in, out, r, path): producers with one and with several K slices,
-# 256-column T blocks, a pair, the skinny kernel (one and several slices)
+# 256-column T blocks, a pair, the skinny kernels (one and several slices,
+# all of K per work-group)
 TIMEOUT_CASES = [
     (1024, 512, 2048, 64, Path.TILED), (300, 1280, 520, 80, Path.TILED), (600, 1024, 1024, 256, Path.TILED),
-    (16, 2048, 4096, 64, Path.SKINNY), (40, 512, 640, 32, Path.SKINNY), (16, 2048, 8192, 128, Path.STREAM),
+    (16, 2048, 4096, 64, Path.SKINNY), (40, 512, 640, 32, Path.SKINNY),
+    (16, 4096, 8192, 64, Path.SKINNY),
 ]
 
 
