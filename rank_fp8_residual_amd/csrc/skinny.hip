@@ -697,14 +697,14 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
 // the kernel's time.
 //
 // T = x B^T comes in pieces: piece (f, ph) is ranks [16 f, +16) over K
-// phase ph (the 256-element chunk ph of every wave's quarter), made by the
-// work-group with id ph * (r_pad / 16) + f, the lowest ids.  A piece
-// work-group starts its rotation at chunk ph, so the piece takes its x from
-// the registers of its first stage; it loads only its B rows, makes the
-// piece before it refills the first ring slot and announces it once the
-// stores are complete (the wait for stage NB).  Every work-group waits for
-// all pieces (long since made) at its end, stages them in LDS and adds them
-// in phase order.
+// phase ph (the 256-element chunks [ph SPP, +SPP) of every wave's quarter),
+// made by the work-group with id ph * (r_pad / 16) + f, the lowest ids.  A
+// piece work-group starts its rotation at chunk ph SPP, so the piece takes
+// its x from the registers of its first SPP stages; it loads only its B
+// rows, makes the piece before it refills the ring after stage SPP - 1 and
+// announces it once the stores are complete.  Every work-group waits for all
+// pieces (long since made) at its end, stages them in LDS and adds them in
+// phase order.
 //
 // The hand-over counts with 64-bit counters that only grow, so nothing has
 // to be reset at the end of a launch (and a captured launch replays
@@ -713,10 +713,10 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
 // the work-groups c with c % 32 == x started.  A work-group's ticket, taken
 // first thing, is L n_x + i for launch L (launches on one workspace run one
 // after another; n_x work-groups per launch share the counter), so this
-// launch's pieces are complete once gen[0] reaches (L + 1) pps.  Spread
-// over 32 counters the tickets' atomics return long before the
-// work-group's first Q stage lands (on one counter, all 256 queue up for
-// microseconds).
+// launch's pieces are complete once gen[0] reaches (L + 1) pps.  The ticket
+// is taken behind the first ring loads, and read once a later stage's wait
+// covers it; spread over 32 counters, the tickets' atomics do not hold up
+// those stages (on one counter all 256 queue up for microseconds).
 //
 // NQ: stages per wave (K quarter = 256 NQ; 4 or 8).
 template <int NQ, int QF>
@@ -725,8 +725,11 @@ __global__ void __launch_bounds__(SNT) skinny_fullk_kernel(SArgs a) {
     constexpr int NB = 4;               // ring slots per wave
     constexpr int STB = 32 * 256;       // bytes per stage
     constexpr int RING = 4 * STB;
-    constexpr int PH = NQ;              // K phases of T (one stage each)
-    constexpr int NP = 8;               // B operands per lane of a piece
+    constexpr int PH = NQ;              // K phases of T (one stage each: the B
+                                        // operands of two would cost the
+                                        // registers that keep the waits exact)
+    constexpr int SPP = NQ / PH;        // stages per phase
+    constexpr int NP = 8 * SPP;         // B operands per lane of a piece
     static_assert(NQ == 4 || NQ == 8, "stages per wave");
     static_assert(PH * 4 * 1024 <= RING, "T pieces of a 64-rank group fit one ring array");
     __shared__ __attribute__((aligned(16))) unsigned char ring0[RING], ring1[RING], ring2[RING], ring3[RING];
@@ -738,14 +741,11 @@ __global__ void __launch_bounds__(SNT) skinny_fullk_kernel(SArgs a) {
     const int c = (int)blockIdx.x;
     const int kq = wave * KQ;
     const int nfrag = a.r_pad / 16;
-    // the ticket (wave 0, lane 0), the first memory operation of the wave
     unsigned long long ticket = 0;
-    if (a.r > 0 && tid == 0)
-        ticket = __hip_atomic_fetch_add(a.gen + 32 * (1 + c % 32), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool has_piece = a.r > 0 && c < a.pps;
     const int pf = has_piece ? c % nfrag : 0, pph = has_piece ? c / nfrag : 0;
     // the first stage of this work-group's rotation
-    const int rot = has_piece ? pph : c % NQ;
+    const int rot = has_piece ? pph * SPP : c % NQ;
 
     // Rows of Q and A behind row l of fragment f (kNoRow: none).  Plain: the
     // product columns [32 c, +32); gated: output columns [16 c, +16), hidden
@@ -800,10 +800,10 @@ __global__ void __launch_bounds__(SNT) skinny_fullk_kernel(SArgs a) {
         }
     u32x4 pb[NP];
     {
-        const int kp = kq + 256 * pph;
+        const int kp = kq + 256 * SPP * pph;
 #pragma unroll
         for (int j = 0; j < NP; ++j) {
-            const int kk = kp + 64 * (j >> 1) + 16 * g + 8 * (j & 1);
+            const int kk = kp + 256 * (j / 8) + 64 * ((j % 8) >> 1) + 16 * g + 8 * (j & 1);
             pb[j] = bload16(rbm, ((unsigned)(16 * pf + l16) * (unsigned)a.K + (unsigned)kk) * 2u +
                                      (has_piece && kk < a.K ? 0u : kOOB));
         }
@@ -853,11 +853,15 @@ __global__ void __launch_bounds__(SNT) skinny_fullk_kernel(SArgs a) {
                (unsigned)__builtin_amdgcn_readfirstlane((unsigned)v);
     };
 
-    // The piece's store goes out in stage 0, after the loads of stage NB - 1
-    // and before those of stage NB: one operation more than the wait for
-    // stage NB - 1 leaves in flight, so that wait covers it (in wave 0, the
-    // one that stores).
-    constexpr int BUMP_AT = NB - 1 < NQ - 1 ? NB - 1 : NQ - 1;
+    // The piece's store goes out in stage SPP - 1, after the loads of stage
+    // SPP + NB - 2 and before those of stage SPP + NB - 1: one operation more
+    // than the wait for stage SPP + NB - 2 leaves in flight, so that wait
+    // covers it (in wave 0, the one that stores).
+    constexpr int BUMP_AT = SPP + NB - 2 < NQ - 1 ? SPP + NB - 2 : NQ - 1;
+    // The ticket goes out in stage 0 right after the loads of stage NB (if
+    // any): the wait for stage NB covers it (one operation more than it
+    // leaves in flight), or the last stage's wait for everything.
+    constexpr int TICKET_READ = NB < NQ ? NB : NQ - 1;
     auto step = [&](auto S) {
         constexpr int s = decltype(S)::value;
         constexpr int later = 16 * ((s + NB < NQ ? s + NB : NQ) - s - 1);
@@ -865,7 +869,7 @@ __global__ void __launch_bounds__(SNT) skinny_fullk_kernel(SArgs a) {
         asm volatile("" ::: "memory");
         if (s == BUMP_AT && has_piece && wave == 0 && lane == 0)
             __hip_atomic_fetch_add(a.gen, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if constexpr (s == NB - 1) {
+        if constexpr (s == TICKET_READ) {
             const unsigned nx = (gridDim.x - (unsigned)(c % 32) + 31) / 32;  // work-groups on this ticket counter
             target = (u64_uniform(ticket) / nx + 1) * (unsigned long long)a.pps + a.t_target;
         }
@@ -883,14 +887,16 @@ __global__ void __launch_bounds__(SNT) skinny_fullk_kernel(SArgs a) {
                 q[f][t] = *reinterpret_cast<const u32x4 *>(st + (16 * f + l16) * 256 + (((4 * t + g) ^ l16) << 4));
         wait_lgkmcnt0();
         asm volatile("" ::: "memory");
-        if constexpr (s == 0) {
+        if constexpr (s == SPP - 1) {
             if (has_piece) {
-                // piece (pf, pph) from the x of stage 0 (chunk pph): the four
-                // waves' quarters added in wave order through LDS by wave 0,
-                // stored as float32 [pph][pf][m][16]
+                // piece (pf, pph) from the x of stages 0 .. SPP - 1 (chunks
+                // pph SPP ..): the four waves' quarters added in wave order
+                // through LDS by wave 0, stored as float32 [pph][pf][m][16]
                 f32x4 tacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < NP; ++j) tacc = mfma16(pb[j], xr[0][j], tacc);
+                for (int i = 0; i < SPP; ++i)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) tacc = mfma16(pb[8 * i + j], xr[i][j], tacc);
                 red[wave * 64 + lane] = tacc;
                 barrier_lds_sync();
                 if (wave == 0) {
@@ -905,6 +911,13 @@ __global__ void __launch_bounds__(SNT) skinny_fullk_kernel(SArgs a) {
             }
         }
         if constexpr (s + NB < NQ) load_stage(s % NB, s + NB);
+        __builtin_amdgcn_sched_barrier(0);
+        // the ticket (wave 0, lane 0), right behind the loads of stage NB
+        if constexpr (s == 0) {
+            if (a.r > 0 && tid == 0)
+                ticket = __hip_atomic_fetch_add(a.gen + 32 * (1 + c % 32), 1ull, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+        }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -942,6 +955,21 @@ __global__ void __launch_bounds__(SNT) skinny_fullk_kernel(SArgs a) {
         }
     }
     barrier_lds_sync();
+    // (ring1, free since its last stage, holds the staged pieces): each wave
+    // stages phases wave, wave + 4, .. of fragments 4 h .. 4 h + 3, 1 KiB each
+    unsigned char *const tst = ring1;
+    auto stage_t = [&](int h) {
+#pragma unroll
+        for (int ph = wave; ph < PH; ph += 4)
+#pragma unroll
+            for (int fr = 0; fr < 4; ++fr) {
+                const bool ok = 4 * h + fr < nfrag && lane < 4 * a.M;
+                bload16_lds<kDeviceCoherent>(rtp, tst + (ph * 4 + fr) * 1024,
+                                             (unsigned)(((ph * nfrag + 4 * h + fr) * a.M * 16) * 4 + lane * 16) +
+                                                 (ok ? 0u : kOOB));
+            }
+    };
+    if (a.r > 0) stage_t(0);  // in flight while wave 0 adds the quarters
     f32x4 sum[WNF];
     if (wave == 0) {
 #pragma unroll
@@ -952,19 +980,7 @@ __global__ void __launch_bounds__(SNT) skinny_fullk_kernel(SArgs a) {
             sum[f] *= a.scale;
         }
     }
-    // (ring1, free since its last stage, holds the staged pieces)
-    unsigned char *const tst = ring1;
     for (int h = 0; h < a.r_pad / 64; ++h) {
-        // phases wave, wave + 4, .. of fragments 4 h .. 4 h + 3: 1 KiB each
-#pragma unroll
-        for (int ph = wave; ph < PH; ph += 4)
-#pragma unroll
-            for (int fr = 0; fr < 4; ++fr) {
-                const bool ok = 4 * h + fr < nfrag && lane < 4 * a.M;
-                bload16_lds<kDeviceCoherent>(rtp, tst + (ph * 4 + fr) * 1024,
-                                             (unsigned)(((ph * nfrag + 4 * h + fr) * a.M * 16) * 4 + lane * 16) +
-                                                 (ok ? 0u : kOOB));
-            }
         wait_vmcnt<0>();
         barrier_lds();
         if (wave == 0) {
@@ -1008,7 +1024,10 @@ __global__ void __launch_bounds__(SNT) skinny_fullk_kernel(SArgs a) {
                 for (int f = 0; f < WNF; ++f) sum[f] = mfma16(af[cc][f], tf, sum[f]);
             }
         }
-        barrier_lds_sync();  // the next group's staging overwrites tst
+        if (h + 1 < a.r_pad / 64) {
+            barrier_lds_sync();  // the next group's staging overwrites tst
+            stage_t(h + 1);
+        }
     }
     if (wave == 0) {
         if (a.glu) {
@@ -1080,7 +1099,7 @@ SkinnyPlan skinny_plan(int64_t M, int64_t K, int64_t N, int64_t r_pad, int64_t s
     // fill most of the chip: all of K per work-group (no K slices).
     const int64_t groups32 = glu ? cdiv64(N / 2, 16) : cdiv64(N, 32);
     const int64_t nq = K <= 4096 ? 4 : 8;
-    const int64_t pieces = (r_pad / 16) * nq;  // 16 ranks x one 256-element chunk of every wave's quarter
+    const int64_t pieces = (r_pad / 16) * nq;  // 16 ranks x one 256-element chunk of every wave's K quarter
     if (pl.mb == 1 && splits_hint <= 0 && K > 2048 && K <= 8192 && groups32 >= 192 && pieces <= groups32 &&
         pieces <= 256) {
         pl.fullk = 1;
