@@ -241,6 +241,21 @@ class Runner:
         torch.cuda.empty_cache()
 
 
+def kernel_name(w, kind):
+    """The kernel function behind a kernel kind on this workload.  The
+    skinny kind has two: skinny_fullk_kernel takes up to 16 rows with
+    2048 < in <= 8192, at least 192 groups of 32 output columns and at most
+    that many T pieces (16 ranks x the K phases: 4 up to in = 4096, else 8),
+    the library's automatic rule restated; skinny_kernel takes the rest."""
+    if kind != "skinny":
+        return KERNEL_NAMES[kind]
+    groups = -(-w.out_features // 32)
+    r_pad = -(-w.rank // 64) * 64 if w.rank else 0
+    pieces = (r_pad // 16) * (4 if w.in_features <= 4096 else 8)
+    fullk = w.M <= 16 and 2048 < w.in_features <= 8192 and groups >= 192 and pieces <= min(groups, 256)
+    return "skinny_fullk_kernel" if fullk else "skinny_kernel"
+
+
 def roofline(w, kt, ms_step, act8=False):
     """Roofline of the dominant kernel.  Its duration per launch is the timed
     region's time per step when the step launches that kernel alone (events
@@ -258,11 +273,12 @@ def roofline(w, kt, ms_step, act8=False):
     else:
         roof = {"bound": "hbm", "achieved": round(by / dur_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    rec = traffic_record(KERNEL_NAMES[dom], w.name + ("+act_fp8" if act8 else ""))
+    kname = kernel_name(w, dom)
+    rec = traffic_record(kname, w.name + ("+act_fp8" if act8 else ""))
     roof["traffic"] = rec["hbm_bytes"] if rec else None
     if rec:
         roof["traffic_detail"] = {k: rec[k] for k in ("fetch_bytes", "write_bytes", "scale", "profile") if k in rec}
-    roof["kernel"] = KERNEL_NAMES[dom]
+    roof["kernel"] = kname
     roof["kernel_us"] = round(dur_s * 1e6, 2)
     roof["kernel_us_event_pairs"] = {k: round(v * 1e3, 2) for k, v in kt.items()}
     roof["algorithmic"] = {"flops": fl, "bytes": by}

@@ -143,7 +143,7 @@ typedef enum {
     LITELINEAR_KERNEL_PAD_A = 0,  /* copy of A into a zero-padded [out, r_pad] buffer (either path,
                                      only when r % 8 != 0 or A is not 16-byte aligned) */
     LITELINEAR_KERNEL_MAIN = 1,   /* tiled path: T = x B^T, residual, rank-r product and bias */
-    LITELINEAR_KERNEL_SKINNY = 2, /* skinny and stream paths: the same in one launch of their own kernel */
+    LITELINEAR_KERNEL_SKINNY = 2, /* skinny path (either skinny kernel): the same in one launch */
     LITELINEAR_KERNEL_QUANT = 3,  /* activations to e4m3fn (LITELINEAR_OPT_ACT_FP8, litelinear_quantize_rows) */
     LITELINEAR_KERNEL_CONVERT = 4 /* decomposition side: litelinear_quantize_tensor, litelinear_residual_quantize
                                      (both passes of one call count as one launch) */

@@ -89,3 +89,16 @@ def test_bench_json_line(tmp_path):
     assert d["clock_ramp"]["ms"] >= 50 and d["clock_ramp"]["steps"] > 0
     probe = d["hbm_read_probe"]
     assert probe["bytes"] == 64 << 20 and 0 < probe["best"]["GB/s"] < 8000
+
+
+def test_kernel_name_follows_the_skinny_rule():
+    """The skinny workload runs the all-of-K kernel; other skinny shapes
+    (more rows, narrow outputs, short or long K) the K-sliced one."""
+    import bench
+    from rank_fp8_residual_amd import workloads as wl
+    assert bench.kernel_name(wl.WORKLOADS["skinny"], "skinny") == "skinny_fullk_kernel"
+    assert bench.kernel_name(wl.WORKLOADS["dit_r64"], "main") == "fused_kernel"
+    import dataclasses
+    W = wl.WORKLOADS["skinny"]
+    for kw in ({"M": 17}, {"out_features": 4096}, {"in_features": 2048}, {"in_features": 16384}):
+        assert bench.kernel_name(dataclasses.replace(W, **kw), "skinny") == "skinny_kernel", kw
