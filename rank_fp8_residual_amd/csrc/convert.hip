@@ -13,8 +13,10 @@
 // like A's, hold 8 consecutive ranks per lane.
 //
 // quant_tensor_kernel does the same two passes for a float32 R given as is.
-// The scale and the quotient R / s are correctly rounded float32 divisions,
-// and the codes come from gfx950's scaled e4m3fn conversion at scale 1.
+// The scale and the quotient R / s are correctly rounded float32 divisions
+// (the quotients through a reciprocal and one exact correction, see
+// Quotient), and the codes come from gfx950's scaled e4m3fn conversion at
+// scale 1.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -40,6 +42,33 @@ __device__ __forceinline__ float scale_of(const unsigned *amax_bits) {
 }
 
 __device__ __forceinline__ float clamp448(float q) { return q > 448.0f ? 448.0f : (q < -448.0f ? -448.0f : q); }
+
+// R / s rounded to float32 (nearest, ties to even) exactly as the IEEE
+// division gives it, for many R and one s.  FAST: in three FMA-unit
+// operations instead of a full division each.  With y = 1/s correctly
+// rounded (one true division), q = R y is within one ulp of R / s, the
+// remainder R - s q is exact in one FMA, and q + (R - s q) y rounded once is
+// the correctly rounded quotient (Markstein's theorem: P. Markstein,
+// "Computation of elementary functions on the IBM RISC System/6000
+// processor", IBM J. Res. Dev. 34(1), 1990).  The theorem needs a remainder
+// free of underflow; for every quotient that can round to a nonzero e4m3fn
+// code (|R / s| >= 2^-10) that holds when s >= 2^-60, so the fast form is
+// only used for 2^-60 <= s <= 2^100 (quotient_fast); elsewhere each
+// quotient is a true division.
+template <bool FAST>
+struct Quotient {
+    float s, y;
+    __device__ explicit Quotient(float s_) : s(s_), y(FAST ? 1.0f / s_ : 0.0f) {}
+    __device__ __forceinline__ float operator()(float r) const {
+        if constexpr (FAST) {
+            const float q = r * y;
+            return __builtin_fmaf(__builtin_fmaf(-q, s, r), y, q);
+        } else {
+            return r / s;
+        }
+    }
+};
+__device__ __forceinline__ bool quotient_fast(float s) { return s >= 0x1p-60f && s <= 0x1p100f; }
 
 // max |v| over a work-group into *amax_bits (non-negative floats order like
 // their bit patterns, so an unsigned atomic max is exact and order-free).
@@ -76,21 +105,28 @@ __global__ void __launch_bounds__(QT_THREADS) quant_tensor_kernel(const float *_
         s = scale_of(amax_bits);
         if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
     }
-    for (int64_t gi = (int64_t)blockIdx.x * QT_THREADS + threadIdx.x; gi < groups;
-         gi += (int64_t)gridDim.x * QT_THREADS) {
-        const f32x4 v = __builtin_bit_cast(f32x4, bload16(rr, (unsigned)(gi * 16)));  // past n: zeros
-        if (!QUANT) {
-            m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-        } else {
-            const unsigned c = codes4(clamp448(v[0] / s), clamp448(v[1] / s), clamp448(v[2] / s), clamp448(v[3] / s));
-            const int64_t i = gi * 4;
-            if (i + 3 < n) {
-                *reinterpret_cast<unsigned *>(codes + i) = c;
+    auto pass = [&](auto div) {
+        for (int64_t gi = (int64_t)blockIdx.x * QT_THREADS + threadIdx.x; gi < groups;
+             gi += (int64_t)gridDim.x * QT_THREADS) {
+            const f32x4 v = __builtin_bit_cast(f32x4, bload16(rr, (unsigned)(gi * 16)));  // past n: zeros
+            if (!QUANT) {
+                m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
             } else {
-                for (int e = 0; e < 4 && i + e < n; ++e) codes[i + e] = (unsigned char)(c >> (8 * e));
+                const unsigned c =
+                    codes4(clamp448(div(v[0])), clamp448(div(v[1])), clamp448(div(v[2])), clamp448(div(v[3])));
+                const int64_t i = gi * 4;
+                if (i + 3 < n) {
+                    *reinterpret_cast<unsigned *>(codes + i) = c;
+                } else {
+                    for (int e = 0; e < 4 && i + e < n; ++e) codes[i + e] = (unsigned char)(c >> (8 * e));
+                }
             }
         }
-    }
+    };
+    if (QUANT && quotient_fast(s))
+        pass(Quotient<QUANT>(s));  // one branch per work-group, no per-element test
+    else
+        pass(Quotient<false>(s));
     if (!QUANT) wg_max(m, amax_bits, red, QT_THREADS / 64);
 }
 
@@ -109,18 +145,21 @@ struct RArgs {
 };
 
 template <bool QUANT>
-__global__ void __launch_bounds__(R_THREADS) residual_kernel(RArgs a) {
+__global__ void __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(3))) residual_kernel(RArgs a) {
     // B's step tile transposed: bt[j][k], 32 ranks (64 bytes) per column,
     // rows padded by 16 bytes so the fragment reads spread over the banks;
     // two of them, for alternate steps.
     constexpr int BTS = RK * 2 + 16;
-    __shared__ __attribute__((aligned(16))) unsigned char bt[2 * RT * BTS];
     // The W tile (rows of RT bf16) and then the tile's codes (rows of RT
     // bytes), both with rows padded by 16 bytes: memory sees whole row
     // segments in 16-byte lanes, the fragments read and write them through
     // LDS (the 16 rows of a fragment fall on distinct banks).
     constexpr int WS = RT * 2 + 16, CS = RT + 16;
-    __shared__ __attribute__((aligned(16))) unsigned char ws[RT * WS];
+    // bt is only used by the product loop and ws only after it, so they
+    // share one array: 35 KiB per work-group, three work-groups per CU.
+    constexpr int LDS_BYTES = 2 * RT * BTS > RT * WS ? 2 * RT * BTS : RT * WS;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+    unsigned char *const bt = lds, *const ws = lds;
     __shared__ unsigned red[R_THREADS / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
     const int tiles_k = (a.K + RT - 1) / RT;
@@ -128,6 +167,12 @@ __global__ void __launch_bounds__(R_THREADS) residual_kernel(RArgs a) {
     const rsrc_t ra = make_rsrc(a.A, (int64_t)a.N * a.r * 2);
     const rsrc_t rb = make_rsrc(a.B, (int64_t)a.r * a.K * 2);
     const rsrc_t rw = make_rsrc(a.W, (int64_t)a.N * a.K * 2);
+    // The second pass requests max |R| first, as a vector load: the tile's
+    // loads queue behind it, and the wait for them covers it.  (A load after
+    // them would wait behind a loaded memory system once more; a scalar
+    // load would hold up the product loop's first LDS wait.)
+    unsigned amax_raw = 0;
+    if constexpr (QUANT) amax_raw = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.amax_bits, 4), 0u, 0, 0);
 
     // The W tile is requested first, 16 bytes per lane along rows (16 lanes
     // per 256-byte row segment, 16 rows per round), and lands while A B is
@@ -206,39 +251,45 @@ __global__ void __launch_bounds__(R_THREADS) residual_kernel(RArgs a) {
         af[1] = an[1];
     }
 
+    __syncthreads();  // the last step's bt reads are done before ws overwrites them
 #pragma unroll
     for (int p = 0; p < WROUNDS; ++p) *reinterpret_cast<u32x4 *>(ws + (16 * p + wrow) * WS + 2 * wcol) = wl[p];
     __syncthreads();
 
     // R = W - A B for the lane's elements: row 32 wave + 16 fr + l16 of the
     // tile, columns 16 fc + 4 g .. + 3.
-    float s = 1.0f, m = 0.0f;
-    if (QUANT) {
-        s = scale_of(a.amax_bits);
-        if (blockIdx.x == 0 && tid == 0) *a.scale_out = s;
-    }
+    const float amax = __builtin_bit_cast(float, amax_raw), s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    float m = 0.0f;
+    if (QUANT && blockIdx.x == 0 && tid == 0) *a.scale_out = s;
     unsigned cv[2][RT / 16];
+    auto residual = [&](auto div) {
 #pragma unroll
-    for (int fr = 0; fr < 2; ++fr) {
-        const int row = 32 * wave + 16 * fr + l16;
-        const bool okn = n0 + row < a.N;
+        for (int fr = 0; fr < 2; ++fr) {
+            const int row = 32 * wave + 16 * fr + l16;
+            const bool okn = n0 + row < a.N;
 #pragma unroll
-        for (int fc = 0; fc < RT / 16; ++fc) {
-            const int col = 16 * fc + 4 * g;
-            const bool ok = okn && j0 + col < a.K;
-            const u32x2 w4 = *reinterpret_cast<const u32x2 *>(ws + row * WS + 2 * col);
-            float rv[4];
+            for (int fc = 0; fc < RT / 16; ++fc) {
+                const int col = 16 * fc + 4 * g;
+                const bool ok = okn && j0 + col < a.K;
+                const u32x2 w4 = *reinterpret_cast<const u32x2 *>(ws + row * WS + 2 * col);
+                float rv[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float w = bf16_to_f32((unsigned short)(w4[v >> 1] >> (16 * (v & 1))));
-                rv[v] = ok ? w - acc[fc][fr][v] : 0.0f;
+                for (int v = 0; v < 4; ++v) {
+                    const float w = bf16_to_f32((unsigned short)(w4[v >> 1] >> (16 * (v & 1))));
+                    rv[v] = ok ? w - acc[fc][fr][v] : 0.0f;
+                }
+                if (!QUANT)
+                    m = fmaxf(m, fmaxf(fmaxf(fabsf(rv[0]), fabsf(rv[1])), fmaxf(fabsf(rv[2]), fabsf(rv[3]))));
+                else
+                    cv[fr][fc] =
+                        codes4(clamp448(div(rv[0])), clamp448(div(rv[1])), clamp448(div(rv[2])), clamp448(div(rv[3])));
             }
-            if (!QUANT)
-                m = fmaxf(m, fmaxf(fmaxf(fabsf(rv[0]), fabsf(rv[1])), fmaxf(fabsf(rv[2]), fabsf(rv[3]))));
-            else
-                cv[fr][fc] = codes4(clamp448(rv[0] / s), clamp448(rv[1] / s), clamp448(rv[2] / s), clamp448(rv[3] / s));
         }
-    }
+    };
+    if (QUANT && quotient_fast(s))
+        residual(Quotient<QUANT>(s));  // one branch per work-group, no per-element test
+    else
+        residual(Quotient<false>(s));
     if (!QUANT) {
         wg_max(m, a.amax_bits, red, R_THREADS / 64);
         return;

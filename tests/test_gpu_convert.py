@@ -41,7 +41,7 @@ def dev():
     return torch.device("cuda", 0)
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(len(quant_arrays()) + 1))
 def test_quantize_tensor_bit_exact(dev, case):
     arrs = quant_arrays() + [np.random.default_rng(8).standard_normal(1 << 22).astype(np.float32) * 3e-3]
     R = arrs[case]

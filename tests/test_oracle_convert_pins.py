@@ -43,6 +43,13 @@ def quant_arrays():
     arrs.append((g.standard_normal(4096) * np.exp2(g.integers(-40, 10, 4096))).astype(np.float32))
     arrs.append(np.zeros(64, np.float32))
     arrs.append(np.array([3.0e-38, -1.0e-30, 7.0], np.float32))
+    # the ties again with amax = 448 2^e, so that the scale is exactly 2^e:
+    # at the ends of and outside the range where a quantiser may divide by
+    # way of a reciprocal (2^-60 .. 2^100), plus random values at those scales
+    t = np.concatenate([np.arange(1, 64) * 2.0 ** e / 16 for e in range(-9, 5)])
+    base = np.concatenate([[448.0], t, -t, g.standard_normal(2048) * 100.0])
+    for e in (-90, -61, -60, 100, 101):
+        arrs.append((base * 2.0 ** e).astype(np.float32))
     return arrs
 
 
