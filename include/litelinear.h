@@ -284,10 +284,14 @@ litelinear_status_t litelinear_quantize_rows(litelinear_handle_t h, const void *
  *   B      bf16 [r, in]   16-byte aligned (may be NULL iff r == 0).
  *   codes  uint8 [out, in] 16-byte aligned; scale_out as above.
  *
- * Both read their input twice (max |R|, then the codes), use one word of
- * the handle's workspace, and are queued on `stream`.  Outputs must not
- * overlap the inputs.  Errors: INVALID_ARG, UNSUPPORTED (alignment, the
- * multiples above, tensors of 2^31 bytes or more), HIP, OOM.
+ * Both read their input twice (max |R|, then the codes) in two launches
+ * queued on `stream`, and use one word of the handle's workspace per
+ * work-group of the first (at most 4096 words for litelinear_quantize_tensor,
+ * one per 128 x 128 tile of W for litelinear_residual_quantize), which the
+ * handle grows as for litelinear_forward (so a captured call must follow an
+ * uncaptured one of at least its size).  Outputs must not overlap the
+ * inputs.  Errors: INVALID_ARG, UNSUPPORTED (alignment, the multiples above,
+ * tensors of 2^31 bytes or more, workspace growth under capture), HIP, OOM.
  */
 litelinear_status_t litelinear_quantize_tensor(litelinear_handle_t h, const float *R, int64_t n, void *codes,
                                                float *scale_out, hipStream_t stream);

@@ -72,7 +72,7 @@ struct DevBuf {
 struct litelinear_ctx {
     int device = 0;
     DevBuf ws[WS_COUNT];
-    DevBuf amax;                    // decomposition side: max |R| as float bits
+    DevBuf amax;                    // decomposition side: per-work-group max |R| (float bits)
     // Error word in host memory mapped into the device: kernels set it when
     // a bounded wait gives up.
     unsigned *err_host = nullptr;
@@ -660,7 +660,7 @@ litelinear_status_t litelinear_quantize_tensor(litelinear_handle_t h, const floa
     DeviceGuard guard(h->device);
     if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
     const bool in_capture = capturing(stream);
-    litelinear_status_t st = grow(h->amax, 256, false, stream, in_capture);
+    litelinear_status_t st = grow(h->amax, (size_t)ll::quant_tensor_slots(n) * 4, false, stream, in_capture);
     if (st != LITELINEAR_OK) return st;
     if (n == 0) {
         const float one = 1.0f;  // scale of an empty (all-zero) tensor
@@ -696,7 +696,8 @@ litelinear_status_t litelinear_residual_quantize(litelinear_handle_t h, const vo
     DeviceGuard guard(h->device);
     if (guard.err != hipSuccess) return LITELINEAR_ERR_HIP;
     const bool in_capture = capturing(stream);
-    litelinear_status_t st = grow(h->amax, 256, false, stream, in_capture);
+    litelinear_status_t st =
+        grow(h->amax, (size_t)ll::residual_quant_slots(out, in) * 4, false, stream, in_capture);
     if (st != LITELINEAR_OK) return st;
     if (out == 0 || in == 0) {
         const float one = 1.0f;

@@ -7,8 +7,11 @@
 //     R = W - A B                      (float32, never stored)
 //     s = max |R| / 448  (1 when R is all zero)
 //     Q = nearest e4m3fn to clamp(R / s, +-448), ties to even
-// in two passes over W: the first reduces max |R| into one device word, the
-// second recomputes R and writes the codes (and s).  A B runs on bf16 matrix
+// in two passes over W: in the first, each work-group writes max |R| over
+// its tile to a slot of its own; in the second, each work-group first takes
+// the maximum over all slots (a few KiB from L2), then recomputes R and
+// writes the codes (and s).  No slot needs clearing between calls and no
+// work-group waits for another, so one call is two launches.  A B runs on bf16 matrix
 // cores (K = r); B's tile is transposed through LDS so that its fragments,
 // like A's, hold 8 consecutive ranks per lane.
 //
@@ -36,9 +39,48 @@ __device__ __forceinline__ unsigned codes4(float a, float b, float c, float d) {
     return __builtin_bit_cast(unsigned, w);
 }
 
-__device__ __forceinline__ float scale_of(const unsigned *amax_bits) {
-    const float amax = __builtin_bit_cast(float, *amax_bits);
+__device__ __forceinline__ float scale_from_amax(unsigned amax_bits) {
+    const float amax = __builtin_bit_cast(float, amax_bits);
     return amax > 0.0f ? amax / 448.0f : 1.0f;
+}
+
+// The per-work-group maxima of the first pass (non-negative floats as bit
+// patterns, which order like the floats): this thread's share, requested
+// with 16-byte loads (slots past `parts` read as zero).  PER: loads per
+// thread, enough for parts <= 4 * PER * threads.
+template <int PER>
+struct PartialMax {
+    u32x4 v[PER];
+    __device__ void request(const unsigned *part, int parts, int tid, int threads) {
+        const rsrc_t r = make_rsrc(part, (int64_t)parts * 4);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[i] = bload16(r, (unsigned)(tid + i * threads) * 16u);
+    }
+    __device__ unsigned thread_max() const {
+        unsigned m = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = v[i][e] > m ? v[i][e] : m;
+        return m;
+    }
+};
+
+// Maximum of u over the work-group (every thread gets it); red holds one
+// word per wave, and the call ends with the work-group's threads in step.
+__device__ __forceinline__ unsigned wg_umax(unsigned u, unsigned *red, int nwaves) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned o = __shfl_xor(u, off);
+        u = o > u ? o : u;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();  // red free (an earlier use is complete)
+    if (lane == 0) red[wave] = u;
+    __syncthreads();
+    unsigned m = 0;
+    for (int w = 0; w < nwaves; ++w) m = red[w] > m ? red[w] : m;
+    return m;
 }
 
 __device__ __forceinline__ float clamp448(float q) { return q > 448.0f ? 448.0f : (q < -448.0f ? -448.0f : q); }
@@ -70,39 +112,30 @@ struct Quotient {
 };
 __device__ __forceinline__ bool quotient_fast(float s) { return s >= 0x1p-60f && s <= 0x1p100f; }
 
-// max |v| over a work-group into *amax_bits (non-negative floats order like
-// their bit patterns, so an unsigned atomic max is exact and order-free).
-__device__ __forceinline__ void wg_max(float v, unsigned *amax_bits, unsigned *red, int nwaves) {
-    unsigned u = __builtin_bit_cast(unsigned, v);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const unsigned o = __shfl_xor(u, off);
-        u = o > u ? o : u;
-    }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) red[wave] = u;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned m = 0;
-        for (int w = 0; w < nwaves; ++w) m = red[w] > m ? red[w] : m;
-        if (m) __hip_atomic_fetch_max(amax_bits, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+// First pass: max |v| over the work-group into its slot part[blockIdx.x].
+__device__ __forceinline__ void wg_max_to_slot(float v, unsigned *part, unsigned *red, int nwaves) {
+    const unsigned m = wg_umax(__builtin_bit_cast(unsigned, v), red, nwaves);
+    if (threadIdx.x == 0) part[blockIdx.x] = m;
 }
 
 // ---------------------------------------------------------- float32 R as is
 
 constexpr int QT_THREADS = 256;
+constexpr int QT_MAX_GRID = 4096;  // both passes run this many work-groups at most
 
+// Both passes run the same grid; part holds one slot per work-group.
 template <bool QUANT>
 __global__ void __launch_bounds__(QT_THREADS) quant_tensor_kernel(const float *__restrict__ R, int64_t n,
-                                                                 unsigned char *__restrict__ codes,
-                                                                 unsigned *amax_bits, float *scale_out) {
+                                                                 unsigned char *__restrict__ codes, unsigned *part,
+                                                                 float *scale_out) {
     __shared__ unsigned red[QT_THREADS / 64];
     const rsrc_t rr = make_rsrc(R, n * 4);
     const int64_t groups = (n + 3) / 4;
     float s = 1.0f, m = 0.0f;
-    if (QUANT) {
-        s = scale_of(amax_bits);
+    if constexpr (QUANT) {
+        PartialMax<QT_MAX_GRID / (4 * QT_THREADS)> pm;
+        pm.request(part, (int)gridDim.x, (int)threadIdx.x, QT_THREADS);
+        s = scale_from_amax(wg_umax(pm.thread_max(), red, QT_THREADS / 64));
         if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
     }
     auto pass = [&](auto div) {
@@ -127,7 +160,7 @@ __global__ void __launch_bounds__(QT_THREADS) quant_tensor_kernel(const float *_
         pass(Quotient<QUANT>(s));  // one branch per work-group, no per-element test
     else
         pass(Quotient<false>(s));
-    if (!QUANT) wg_max(m, amax_bits, red, QT_THREADS / 64);
+    if (!QUANT) wg_max_to_slot(m, part, red, QT_THREADS / 64);
 }
 
 // ------------------------------------------------------- R = W - A B on MFMA
@@ -139,10 +172,13 @@ constexpr int R_THREADS = 256; // 4 waves, wave w owns rows 32 w .. 32 w + 31
 struct RArgs {
     const unsigned char *W, *A, *B;
     unsigned char *codes;
-    unsigned *amax_bits;
+    unsigned *part;  // one slot per tile (work-group)
     float *scale_out;
     int N, K, r;  // W is [N, K], A [N, r], B [r, K]
+    int parts;    // tiles
 };
+
+constexpr int R_PART_PER = 4;  // slot loads per thread issued ahead (4096 slots; more are read in a loop)
 
 template <bool QUANT>
 __global__ void __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(3))) residual_kernel(RArgs a) {
@@ -167,12 +203,10 @@ __global__ void __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
     const rsrc_t ra = make_rsrc(a.A, (int64_t)a.N * a.r * 2);
     const rsrc_t rb = make_rsrc(a.B, (int64_t)a.r * a.K * 2);
     const rsrc_t rw = make_rsrc(a.W, (int64_t)a.N * a.K * 2);
-    // The second pass requests max |R| first, as a vector load: the tile's
-    // loads queue behind it, and the wait for them covers it.  (A load after
-    // them would wait behind a loaded memory system once more; a scalar
-    // load would hold up the product loop's first LDS wait.)
-    unsigned amax_raw = 0;
-    if constexpr (QUANT) amax_raw = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.amax_bits, 4), 0u, 0, 0);
+    // The second pass requests the first pass's slots before the tile: the
+    // tile's loads queue behind them, and the wait for those covers them.
+    PartialMax<R_PART_PER> pm;
+    if constexpr (QUANT) pm.request(a.part, a.parts, tid, R_THREADS);
 
     // The W tile is requested first, 16 bytes per lane along rows (16 lanes
     // per 256-byte row segment, 16 rows per round), and lands while A B is
@@ -222,6 +256,18 @@ __global__ void __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
         load_b(0, bv);
         load_a(0, af);
     }
+    // This thread's maximum over its slots (the wait covers only them: they
+    // were requested first); slots past those requested ahead, in a loop.
+    unsigned pmax = 0;
+    if constexpr (QUANT) {
+        pmax = pm.thread_max();
+        const rsrc_t rp = make_rsrc(a.part, (int64_t)a.parts * 4);
+        for (int q = R_PART_PER * R_THREADS + tid; q < (a.parts + 3) / 4; q += R_THREADS) {
+            const u32x4 v = bload16(rp, (unsigned)q * 16u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pmax = v[e] > pmax ? v[e] : pmax;
+        }
+    }
     for (int k0 = 0, st = 0; k0 < a.r; k0 += RK, st ^= 1) {
         if (k0 + RK < a.r) {
             load_b(k0 + RK, bn);
@@ -258,7 +304,7 @@ __global__ void __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
 
     // R = W - A B for the lane's elements: row 32 wave + 16 fr + l16 of the
     // tile, columns 16 fc + 4 g .. + 3.
-    const float amax = __builtin_bit_cast(float, amax_raw), s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    const float s = QUANT ? scale_from_amax(wg_umax(pmax, red, R_THREADS / 64)) : 1.0f;
     float m = 0.0f;
     if (QUANT && blockIdx.x == 0 && tid == 0) *a.scale_out = s;
     unsigned cv[2][RT / 16];
@@ -291,7 +337,7 @@ __global__ void __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
     else
         residual(Quotient<false>(s));
     if (!QUANT) {
-        wg_max(m, a.amax_bits, red, R_THREADS / 64);
+        wg_max_to_slot(m, a.part, red, R_THREADS / 64);
         return;
     }
     // Codes: into LDS in fragment order (over the W tile, once every wave
@@ -316,40 +362,43 @@ __global__ void __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
 
 }  // namespace
 
-hipError_t launch_quant_tensor(const float *R, int64_t n, void *codes, unsigned *amax_bits, float *scale_out,
+int64_t quant_tensor_slots(int64_t n) {
+    const int64_t blocks = ((n + 3) / 4 + QT_THREADS - 1) / QT_THREADS;
+    return blocks < 1 ? 1 : (blocks < QT_MAX_GRID ? blocks : QT_MAX_GRID);
+}
+
+int64_t residual_quant_slots(int64_t N, int64_t K) { return ((N + RT - 1) / RT) * ((K + RT - 1) / RT); }
+
+hipError_t launch_quant_tensor(const float *R, int64_t n, void *codes, unsigned *part, float *scale_out,
                                hipStream_t s) {
     if (n <= 0) return hipSuccess;
     if (n * 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    const int64_t groups = (n + 3) / 4;
-    const int grid = (int)((groups + QT_THREADS - 1) / QT_THREADS < 4096 ? (groups + QT_THREADS - 1) / QT_THREADS : 4096);
-    hipError_t e = launch_fill_u32(amax_bits, 1, 0u, s);
-    if (e != hipSuccess) return e;
+    const int grid = (int)quant_tensor_slots(n);
     hipLaunchKernelGGL(quant_tensor_kernel<false>, dim3(grid), dim3(QT_THREADS), 0, s, R, n,
-                       (unsigned char *)codes, amax_bits, scale_out);
+                       (unsigned char *)codes, part, scale_out);
     hipLaunchKernelGGL(quant_tensor_kernel<true>, dim3(grid), dim3(QT_THREADS), 0, s, R, n,
-                       (unsigned char *)codes, amax_bits, scale_out);
+                       (unsigned char *)codes, part, scale_out);
     return hipGetLastError();
 }
 
 hipError_t launch_residual_quant(const void *W, const void *A, const void *B, int64_t N, int64_t K, int64_t r,
-                                 void *codes, unsigned *amax_bits, float *scale_out, hipStream_t s) {
+                                 void *codes, unsigned *part, float *scale_out, hipStream_t s) {
     if (N <= 0 || K <= 0) return hipSuccess;
     const int64_t lim = (int64_t)1 << 31;
     if (N * K * 2 >= lim || N * r * 2 >= lim || r * K * 2 >= lim) return hipErrorInvalidValue;
+    const int64_t tiles = residual_quant_slots(N, K);
+    if (tiles >= lim / 4) return hipErrorInvalidValue;
     RArgs a{};
     a.W = (const unsigned char *)W;
     a.A = (const unsigned char *)A;
     a.B = (const unsigned char *)B;
     a.codes = (unsigned char *)codes;
-    a.amax_bits = amax_bits;
+    a.part = part;
     a.scale_out = scale_out;
     a.N = (int)N;
     a.K = (int)K;
     a.r = (int)r;
-    const int64_t tiles = ((N + RT - 1) / RT) * ((K + RT - 1) / RT);
-    if (tiles >= lim) return hipErrorInvalidValue;
-    hipError_t e = launch_fill_u32(amax_bits, 1, 0u, s);
-    if (e != hipSuccess) return e;
+    a.parts = (int)tiles;
     hipLaunchKernelGGL(residual_kernel<false>, dim3((unsigned)tiles), dim3(R_THREADS), 0, s, a);
     hipLaunchKernelGGL(residual_kernel<true>, dim3((unsigned)tiles), dim3(R_THREADS), 0, s, a);
     return hipGetLastError();

@@ -47,15 +47,18 @@ struct TiledProblem {
 hipError_t launch_quant_rows(const void *x, int64_t ldx, void *codes, float *scales, int64_t M, int64_t K,
                              hipStream_t s);
 
-// Decomposition side (convert.hip).  amax_bits: one device word of
-// workspace, cleared on the stream by each call.
+// Decomposition side (convert.hip).  part: workspace of *_slots() words
+// (one per work-group of the first pass), written before it is read in
+// each call, so it needs no clearing.
+int64_t quant_tensor_slots(int64_t n);
+int64_t residual_quant_slots(int64_t N, int64_t K);
 // float32 R [n] (n % 4 == 0) -> codes [n], *scale_out = max|R| / 448.
-hipError_t launch_quant_tensor(const float *R, int64_t n, void *codes, unsigned *amax_bits, float *scale_out,
+hipError_t launch_quant_tensor(const float *R, int64_t n, void *codes, unsigned *part, float *scale_out,
                                hipStream_t s);
 // R = W - A B (W bf16 [N, K], A bf16 [N, r], B bf16 [r, K]; K % 16 == 0,
 // r % 8 == 0) -> codes [N, K], *scale_out = max|R| / 448.
 hipError_t launch_residual_quant(const void *W, const void *A, const void *B, int64_t N, int64_t K, int64_t r,
-                                 void *codes, unsigned *amax_bits, float *scale_out, hipStream_t s);
+                                 void *codes, unsigned *part, float *scale_out, hipStream_t s);
 
 // HBM read ceiling probe (probe.hip): reads bytes (a multiple of 16) of src
 // once with `wgs` work-groups of 256 threads, `unroll` (4, 8 or 16) 16-byte

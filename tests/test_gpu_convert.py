@@ -100,6 +100,25 @@ def test_residual_quantize_parity(dev, shape):
     assert np.mean(c != c_ref) <= 1e-3, np.mean(c != c_ref)
 
 
+def test_residual_quantize_max_in_last_of_many_tiles(dev):
+    """More 128 x 128 tiles (65 x 64) than the second pass requests slots
+    ahead for (4096): the largest |R| sits in the last tile, whose slot only
+    the remainder loop reads."""
+    out, K, r = 8320, 8192, 8
+    W, A, B = _inputs(out, K, r, seed=41)
+    W[-1, -1] = 8.0
+    say("residual_quantize", (out, K, r), "max in the last tile")
+    R = oracle.residual(W, A, B)
+    c_ref, s_ref = oracle.quantize_tensor(R.astype(np.float32))
+    codes, scale = Handle(dev.index).residual_quantize(W.to(dev), A.to(dev), B.to(dev))
+    torch.cuda.synchronize()
+    s = float(scale.item())
+    assert abs(s - s_ref) <= 2 * np.spacing(np.float32(s_ref)), (s, s_ref)
+    c = codes.cpu().numpy()
+    assert np.all(_neighbours(c, c_ref))
+    assert np.mean(c != c_ref) <= 1e-3
+
+
 def test_residual_quantize_exact_products_bit_exact(dev):
     W, A, B = _inputs(300, 512, 32, seed=5, exact=True)
     R = oracle.residual(W, A, B)
