@@ -56,6 +56,26 @@ def test_quantize_tensor_bit_exact(dev, case):
     assert bad.size == 0, (R[bad[:5]], c[bad[:5]], c_ref[bad[:5]])
 
 
+def test_quantize_tensor_max_in_every_lane(dev):
+    """The first pass reduces max |R| per wave (64 lanes) and work-group: a
+    single largest value placed in each lane of the first and last wave of
+    one work-group (four values per lane) sets the scale every time."""
+    n = 3 * 256 * 4  # three work-groups of 256 threads, four values each
+    base = np.random.default_rng(11).standard_normal(n).astype(np.float32) * 0.01
+    h = Handle(dev.index)
+    say("quantize_tensor max in every lane")
+    for wave in (0, 3):
+        for lane in range(64):
+            R = base.copy()
+            i = (256 + 64 * wave + lane) * 4 + lane % 4  # work-group 1
+            R[i] = -7.5 if lane % 2 else 7.5
+            c_ref, s_ref = oracle.quantize_tensor(R)
+            codes, scale = h.quantize_tensor(torch.from_numpy(R).to(dev))
+            torch.cuda.synchronize()
+            assert float(scale.item()) == s_ref, (wave, lane)
+            assert np.array_equal(codes.cpu().numpy(), c_ref), (wave, lane)
+
+
 def _inputs(out, K, r, seed, exact=False):
     g = torch.Generator().manual_seed(seed)
     if exact:
