@@ -127,6 +127,21 @@ __device__ __forceinline__ u32x2 q8x4_to_bf16x4(unsigned w) {
     }
 }
 
+// Maximum of u over the wave (every lane gets it): within each row of 16
+// lanes a running maximum from lanes 1, 2, 4, 8 below (DPP row shifts,
+// lanes without a source keep their value), which leaves each row's maximum
+// in its lane 15, then the four rows' lanes 15 combined as scalars.
+__device__ __forceinline__ unsigned wave_umax(unsigned u) {
+    auto up = [](unsigned a, unsigned b) { return a > b ? a : b; };
+    u = up(u, (unsigned)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x111, 0xF, 0xF, false));  // row_shr:1
+    u = up(u, (unsigned)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x112, 0xF, 0xF, false));  // row_shr:2
+    u = up(u, (unsigned)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x114, 0xF, 0xF, false));  // row_shr:4
+    u = up(u, (unsigned)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x118, 0xF, 0xF, false));  // row_shr:8
+    const unsigned r0 = (unsigned)__builtin_amdgcn_readlane((int)u, 15), r1 = (unsigned)__builtin_amdgcn_readlane((int)u, 31);
+    const unsigned r2 = (unsigned)__builtin_amdgcn_readlane((int)u, 47), r3 = (unsigned)__builtin_amdgcn_readlane((int)u, 63);
+    return up(up(r0, r1), up(r2, r3));
+}
+
 // True on every lane when `p` holds on any lane of the wave.
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 

@@ -82,11 +82,12 @@ __global__ void __launch_bounds__(QWAVES * 64) quant_rows_kernel(const unsigned 
     } else {
         for (int k0 = 0; k0 < K; k0 += 512) scan(load(k0 + 8 * lane));
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const unsigned o = __shfl_xor(amax, off);
-        amax = o > amax ? o : amax;
-        bad |= __shfl_xor(bad, off);
+    // one wave maximum of (bad, amax): bit 16 set if any lane saw a
+    // non-finite value, and then the row gets e = 0 whatever amax is
+    {
+        const unsigned key = wave_umax((bad << 16) | amax);
+        bad = key >> 16;
+        amax = key & 0xFFFFu;
     }
     // Scale exponent: amax = mant 2^ex with mant in [0.5, 1); 448 2^e is
     // 0.875 2^(e + 9).  A bf16 pattern below 0x0080 (subnormal) is under
