@@ -110,10 +110,24 @@ def mfma_peak(w, act8: bool) -> float:
     return (f8 + f16) / (f8 / PEAK_FP8_TFLOPS + f16 / PEAK_BF16_TFLOPS)
 
 
-def source_digest() -> str:
-    """sha256 over the kernel sources: a counter record applies only to them."""
+# The sources that make up each kernel as launched: its own file, the
+# shared device helpers and launch declarations, and the host code that
+# chooses its variant and launch shape.
+KERNEL_SOURCES = {
+    "fused_kernel": ("tiled.hip", "device_common.hpp", "launch.hpp", "api.cpp"),
+    "skinny_fullk_kernel": ("skinny.hip", "device_common.hpp", "launch.hpp", "api.cpp"),
+    "skinny_kernel": ("skinny.hip", "device_common.hpp", "launch.hpp", "api.cpp"),
+}
+
+
+def source_digest(kernel: str | None = None) -> str:
+    """sha256 over a kernel's sources (all of csrc/ without a kernel name): a
+    counter record applies only to the sources it was taken on."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "rank_fp8_residual_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "rank_fp8_residual_amd", "csrc")
+    names = KERNEL_SOURCES.get(kernel) if kernel else None
+    files = [os.path.join(csrc, n) for n in names] if names else glob.glob(os.path.join(csrc, "*"))
+    for f in sorted(files):
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
             h.update(fh.read())
@@ -122,8 +136,8 @@ def source_digest() -> str:
 
 def traffic_record(kernel: str, workload: str):
     """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current kernel sources."""
-    digest = source_digest()
+    on the current sources of that kernel."""
+    digest = source_digest(kernel)
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for line in open(f):
             if not line.startswith("traffic-record:"):

@@ -11,9 +11,9 @@
 // its tile to a slot of its own; in the second, each work-group first takes
 // the maximum over all slots (a few KiB from L2), then recomputes R and
 // writes the codes (and s).  No slot needs clearing between calls and no
-// work-group waits for another, so one call is two launches.  A B runs on bf16 matrix
-// cores (K = r); B's tile is transposed through LDS so that its fragments,
-// like A's, hold 8 consecutive ranks per lane.
+// work-group waits for another, so one call is two launches.  A B runs on
+// bf16 matrix cores (K = r); B's tile is transposed through LDS so that its
+// fragments, like A's, hold 8 consecutive ranks per lane.
 //
 // quant_tensor_kernel does the same two passes for a float32 R given as is.
 // The scale and the quotient R / s are correctly rounded float32 divisions

@@ -102,3 +102,13 @@ def test_kernel_name_follows_the_skinny_rule():
     W = wl.WORKLOADS["skinny"]
     for kw in ({"M": 17}, {"out_features": 4096}, {"in_features": 2048}, {"in_features": 16384}):
         assert bench.kernel_name(dataclasses.replace(W, **kw), "skinny") == "skinny_kernel", kw
+
+
+def test_kernel_sources_exist():
+    """Every file a traffic record's digest covers is a library source."""
+    import bench
+    csrc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "rank_fp8_residual_amd", "csrc")
+    for kernel, names in bench.KERNEL_SOURCES.items():
+        for n in names:
+            assert os.path.isfile(os.path.join(csrc, n)), (kernel, n)
+        assert bench.source_digest(kernel) != bench.source_digest()
