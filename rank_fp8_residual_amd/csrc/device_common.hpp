@@ -214,6 +214,14 @@ __device__ __forceinline__ float bload_bf16(rsrc_t r, unsigned n) {
 // a whole L2.
 constexpr int kCached = 0;
 constexpr int kDeviceCoherent = 16;
+// Streamed once (the nt bit): the lines are not kept for reuse, which leaves
+// the caches to data that is read again.
+constexpr int kNonTemporal = 2;
+
+// bload16 for data read exactly once (kNonTemporal).
+__device__ __forceinline__ u32x4 bload16_nt(rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
+}
 
 // 16 bytes per lane from the buffer straight into LDS: lane l's bytes land at
 // lds + 16 * l (lds is wave-uniform).  Counts against vmcnt like any load.

@@ -574,7 +574,7 @@ __global__ void __launch_bounds__(SNT) skinny_kernel(SArgs a) {
         const int k = kb + 64 * s + 16 * g;
         const unsigned oob = k < a.K ? 0u : kOOB;
 #pragma unroll
-        for (int f = 0; f < WNF; ++f) q[f] = bload16(rq, qoff[f] + (unsigned)k + oob);
+        for (int f = 0; f < WNF; ++f) q[f] = bload16_nt(rq, qoff[f] + (unsigned)k + oob);
     };
     u32x4 qr[D][WNF];
 #pragma unroll
@@ -829,7 +829,7 @@ __global__ void __launch_bounds__(SNT) skinny_fullk_kernel(SArgs a) {
             const int k = k0 + 16 * (ls ^ l);
             const unsigned row = row_of(R >> 4, l);
             const unsigned off = row == kNoRow || k >= a.K ? kOOB : row * (unsigned)a.K + (unsigned)k;
-            bload16_lds(rq, slot_ptr(slot) + 1024 * i, off);
+            bload16_lds<kNonTemporal>(rq, slot_ptr(slot) + 1024 * i, off);
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) xr[s][j] = bload16(rx, xoff(k0, j));
