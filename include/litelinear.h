@@ -135,7 +135,20 @@ typedef enum {
      * decoded exactly either way.  e4m3fnuz runs with bf16 activations only
      * (with LITELINEAR_OPT_ACT_FP8 the forward returns UNSUPPORTED) and on
      * output tiles of at most 256 x 128. */
-    LITELINEAR_OPT_Q_FORMAT = 9
+    LITELINEAR_OPT_Q_FORMAT = 9,
+    /* Tiled path: how T = x B^T is computed.  0 = choose automatically
+     * (default); 1 = by producer work-groups inside the output tiles' launch
+     * (they hold back some output tiles until T is done); 2 = by a launch of
+     * its own queued just before, where the shape allows it: r <= 128,
+     * in <= 8192 (4096 for r > 64), T handed over through memory in
+     * 64-column blocks (not for ranks that are multiples of 256 on 256 x 256
+     * tiles, nor where tiny problems compute T inside each output tile);
+     * otherwise as 1.  Automatic: a launch of its own for
+     * grids of fewer than four rounds of one output tile per compute unit
+     * whose last round has no free slots for the producers.  Either way T'
+     * is the same float32 sum rounded once; only its order of additions
+     * differs. */
+    LITELINEAR_OPT_T_LAUNCH = 10
 } litelinear_option_t;
 
 /* Kernels whose time litelinear_kernel_time() reports. */

@@ -79,8 +79,8 @@ struct litelinear_ctx {
     unsigned *err_dev = nullptr;
     bool sync_dirty = false;        // counters must be cleared before the next launch
     void *scratch = nullptr;        // the device's fixed scratch (litelinear_forward_noalloc)
-    int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0, opt_t_splits = 0, opt_act_fp8 = 0,
-            opt_gelu = 0, opt_test_wait = 0, opt_q_format = 0;
+    int64_t opt_path = 0, opt_out_f32 = 0, opt_split = 0, opt_profile = 0, opt_t_splits = 0, opt_t_launch = 0,
+            opt_act_fp8 = 0, opt_gelu = 0, opt_test_wait = 0, opt_q_format = 0;
     Prof prof[kNumKernels];
     std::vector<hipEvent_t> event_pool;
 };
@@ -260,6 +260,10 @@ litelinear_status_t litelinear_set_option(litelinear_handle_t h, int key, int64_
         case LITELINEAR_OPT_T_SPLITS:
             if (value < 0 || value > 64) return LITELINEAR_ERR_INVALID_ARG;
             h->opt_t_splits = value;
+            return LITELINEAR_OK;
+        case LITELINEAR_OPT_T_LAUNCH:
+            if (value < 0 || value > 2) return LITELINEAR_ERR_INVALID_ARG;
+            h->opt_t_launch = value;
             return LITELINEAR_OK;
         case LITELINEAR_OPT_ACT_FP8:
             if (value != 0 && value != 1) return LITELINEAR_ERR_INVALID_ARG;
@@ -472,8 +476,10 @@ litelinear_status_t forward_impl(litelinear_ctx *h, const void *x, int64_t ldx, 
         if (producers) {
             rq.need[WS_TWS] = (size_t)M * r_pad * 2;
             if (s2) rq.need[WS_TWS2] = (size_t)M * r_pad * 2;
-            p.t_splits = ll::tiled_t_splits(p, mc, h->opt_t_splits);
-            if (p.t_splits > 1) rq.need[WS_TPART] = (size_t)p.t_splits * M * r_pad * sizeof(float);
+            p.t_launch = ll::tiled_t_launch(p, mc, h->opt_t_launch);
+            p.t_splits = p.t_launch > 0 ? 1 : ll::tiled_t_splits(p, mc, h->opt_t_splits);
+            const int parts = p.t_launch > 0 ? p.t_launch : p.t_splits;
+            if (parts > 1) rq.need[WS_TPART] = (size_t)parts * M * r_pad * sizeof(float);
             rq.need[WS_SYNC] = (size_t)ll::tiled_sync_words(p, mc) * sizeof(unsigned);
         }
     }

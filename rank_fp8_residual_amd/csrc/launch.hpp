@@ -18,6 +18,8 @@ struct TiledProblem {
     int64_t M, K, N, r, r_pad;
     int64_t ldx;         // elements between rows of x (>= K, multiple of 8)
     int t_splits;        // K slices per T block (tiled_t_splits())
+    int t_launch;        // K slices of T's launch of its own (tiled_t_launch()),
+                         // 0: T producers inside the output tiles' launch
     unsigned *err;       // host-visible error word (a bounded wait gave up)
     unsigned wait_limit; // polls before a bounded wait gives up (> 0)
     unsigned wait_extra; // added to every wait's target: 0, or 1 to make the
@@ -98,10 +100,19 @@ hipError_t launch_fill_u32(unsigned *p, int64_t n, unsigned v, hipStream_t s);
 // early but few enough to leave most CUs to the output tiles.
 // hint > 0 asks for that many slices (capped at the number of K steps).
 int tiled_t_splits(const TiledProblem &p, TileCfg c, int64_t hint);
+// T in a launch of its own, queued before the output tiles' launch, instead
+// of producer work-groups inside it: for grids of fewer than four rounds
+// whose last round has no free slots for the producers.  Needs 64-column T
+// blocks, r_pad <= 128 and in <= 8192 (4096 for r_pad = 128).  Returns its
+// K slices (t_part holds that many partial sums when more than one), or 0
+// for in-launch producers.  hint: 0 = automatic, 1 = in-launch producers,
+// 2 = a launch of its own wherever the shape allows it.
+int tiled_t_launch(const TiledProblem &p, TileCfg c, int64_t hint);
 // sync: tiled_sync_words() counters, zero before the launch and zero again
 // after it: per row tile the T blocks finished (tiled_flag_step() of them
 // complete the row tile's T) and the consumers done reading T' (the last one
 // clears both), per T block the finished K slices (the last slice clears it).
+// Covers both ways of computing T (p.t_launch).
 int64_t tiled_sync_words(const TiledProblem &p, TileCfg c);
 unsigned tiled_flag_step(const TiledProblem &p, TileCfg c);
 // True when the output work-groups compute T themselves (no producers, no

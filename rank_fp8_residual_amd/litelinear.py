@@ -42,6 +42,7 @@ class Option(enum.IntEnum):
     ACTIVATION = 7  # 1 = GELU (tanh approximation) on y, fused into the epilogue
     TEST_WAIT_TIMEOUT = 8  # test hook: n > 0 makes every bounded wait give up after n polls
     Q_FORMAT = 9  # residual codes: 0 e4m3fn, 1 e4m3fnuz
+    T_LAUNCH = 10  # tiled path: T by 0 = automatic choice, 1 = in-launch producers, 2 = a launch of its own
 
 
 class Activation(enum.IntEnum):
