@@ -476,7 +476,8 @@ def test_bad_arguments_return_status(dev):
         h.forward(d2["x"], d2["A"], d2["B"], d2["Q"], d2["scale"], d2["bias"])
     assert e.value.status == Status.UNSUPPORTED
     for key, bad in ((Option.PATH, 3), (Option.OUTPUT_F32, 2), (Option.SPLIT_K, -1), (Option.PROFILE, 5),
-                     (Option.T_SPLITS, 65), (Option.T_SPLITS, -1), (99, 0)):
+                     (Option.T_SPLITS, 65), (Option.T_SPLITS, -1), (Option.T_LAUNCH, 3), (Option.T_LAUNCH, -1),
+                     (99, 0)):
         with pytest.raises(LiteLinearError) as e:
             h.set_option(key, bad)
         assert e.value.status == Status.INVALID_ARG
