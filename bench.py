@@ -78,6 +78,8 @@ def parse():
     p.add_argument("--path", default="auto", choices=["auto", "skinny", "tiled"])
     p.add_argument("--split-k", type=int, default=0, help="skinny path: K-slice hint (0: automatic)")
     p.add_argument("--t-splits", type=int, default=0, help="tiled path: K slices per T block (0: automatic)")
+    p.add_argument("--t-launch", type=int, default=0, choices=[0, 1, 2],
+                   help="tiled path: how T is computed (the T_LAUNCH option; 0: automatic)")
     p.add_argument("--act-fp8", action="store_true",
                    help="e4m3fn activations for the residual product (LITELINEAR_OPT_ACT_FP8)")
     return p.parse_args()
@@ -175,6 +177,7 @@ class Runner:
         self.h.set_option(Option.PATH, {"auto": Path.AUTO, "skinny": Path.SKINNY, "tiled": Path.TILED}[args.path])
         self.h.set_option(Option.SPLIT_K, args.split_k)
         self.h.set_option(Option.T_SPLITS, args.t_splits)
+        self.h.set_option(Option.T_LAUNCH, args.t_launch)
         self.act8 = args.act_fp8 if act8 is None else act8
         self.h.set_option(Option.ACT_FP8, int(self.act8))
         self.dev = dev

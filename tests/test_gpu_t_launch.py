@@ -170,15 +170,18 @@ def test_t_launch_pair(dev):
         parity.check(parity.to_f64(y2), oracle_y(d2), False)
 
 
-def test_t_launch_graph_capture(dev):
+@pytest.mark.parametrize("act8", [False, True], ids=["bf16", "act8"])
+def test_t_launch_graph_capture(dev, act8):
     """Captured with the T launch, replayed on new inputs with eager work in
-    between: every replay matches the oracle."""
+    between: every replay matches the oracle, with bf16 and with e4m3fn
+    activations (the quantiser, the T launch and the output tiles)."""
     M, K, N, r = 1024, 2048, 2048, 64
     d0 = wl.random_inputs(M, K, N, r, seed=7500)
     g = to_dev(d0, dev)
     h = handle(dev, 2)
+    h.set_option(Option.ACT_FP8, int(act8))
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    say("t launch capture")
+    say("t launch capture", "act8" if act8 else "bf16")
     fwd(h, g, out=y)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -186,6 +189,7 @@ def test_t_launch_graph_capture(dev):
         fwd(h, g, out=y)
     torch.cuda.synchronize()
     other = handle(dev, 2)
+    other.set_option(Option.ACT_FP8, int(act8))
     for seed in (7501, 7502, 7503):
         d = wl.random_inputs(M, K, N, r, seed=seed)
         d["scale"] = d0["scale"]
@@ -194,10 +198,11 @@ def test_t_launch_graph_capture(dev):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        parity.check(parity.to_f64(y), oracle_y(d), False)
+        y_ref = oracle_y(d, act_fp8=act8)
+        parity.check(parity.to_f64(y), y_ref, False)
         ye = fwd(other, g)
         torch.cuda.synchronize()
-        parity.check(parity.to_f64(ye), oracle_y(d), False)
+        parity.check(parity.to_f64(ye), y_ref, False)
     del graph
 
 
