@@ -246,11 +246,19 @@ __global__ void __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
             af[fr] = bload16(ra, ((unsigned)n * (unsigned)a.r + (unsigned)k) * 2u + (n < a.N && k < a.r ? 0u : kOOB));
         }
     };
-    u32x2 bv[4], bn[4];
-    u32x4 af[2], an[2];
+    // Two register sets, each refilled for the step two ahead as soon as its
+    // contents are consumed (B's into LDS, A's into the products), so every
+    // load has two steps of work to land behind.  (A copy from a set loaded
+    // for the next step into the current one would wait for that load.)
+    u32x2 bv0[4], bv1[4];
+    u32x4 af0[2], af1[2];
     if (a.r > 0) {
-        load_b(0, bv);
-        load_a(0, af);
+        load_b(0, bv0);
+        load_a(0, af0);
+    }
+    if (a.r > RK) {
+        load_b(RK, bv1);
+        load_a(RK, af1);
     }
     // This thread's maximum over its slots (the wait covers only them: they
     // were requested first); slots past those requested ahead, in a loop.
@@ -264,11 +272,7 @@ __global__ void __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
             for (int e = 0; e < 4; ++e) pmax = v[e] > pmax ? v[e] : pmax;
         }
     }
-    for (int k0 = 0, st = 0; k0 < a.r; k0 += RK, st ^= 1) {
-        if (k0 + RK < a.r) {
-            load_b(k0 + RK, bn);
-            load_a(k0 + RK, an);
-        }
+    auto step = [&](int k0, int st, u32x2 (&bv)[4], u32x4 (&af)[2]) {
         // bt[st] was last read two steps ago, before the previous step's barrier.
         unsigned char *const b = bt + st * (RT * BTS);
 #pragma unroll
@@ -280,6 +284,7 @@ __global__ void __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
                                       : (bv[2][c >> 1] & 0xFFFFu) | (bv[3][c >> 1] << 16);
             *reinterpret_cast<u32x2 *>(b + (jq + c) * BTS + kq * 2) = u32x2{lo, hi};
         }
+        if (k0 + 2 * RK < a.r) load_b(k0 + 2 * RK, bv);
         __syncthreads();
 #pragma unroll
         for (int fc = 0; fc < RT / 16; ++fc) {
@@ -287,10 +292,11 @@ __global__ void __launch_bounds__(R_THREADS) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int fr = 0; fr < 2; ++fr) acc[fc][fr] = mfma16(bf, af[fr], acc[fc][fr]);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bv[e] = bn[e];
-        af[0] = an[0];
-        af[1] = an[1];
+        if (k0 + 2 * RK < a.r) load_a(k0 + 2 * RK, af);
+    };
+    for (int k0 = 0; k0 < a.r; k0 += 2 * RK) {
+        step(k0, 0, bv0, af0);
+        if (k0 + RK < a.r) step(k0 + RK, 1, bv1, af1);
     }
 
     __syncthreads();  // the last step's bt reads are done before ws overwrites them
